@@ -1,0 +1,32 @@
+"""CPU fp64 oracle for calibrated block-sparse attention -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The GPU library never calls it and shares no code with it.
+"""
+from .calibattn_oracle import (
+    dense_attention,
+    block_energy,
+    select_row,
+    select_blocks,
+    aggregate_votes,
+    build_csr,
+    computed_rows,
+    sparse_attention,
+    row_broadcast,
+    sparse_attention_with_repetition,
+    token_mask_from_blocks,
+)
+
+__all__ = [
+    "dense_attention",
+    "block_energy",
+    "select_row",
+    "select_blocks",
+    "aggregate_votes",
+    "build_csr",
+    "computed_rows",
+    "sparse_attention",
+    "row_broadcast",
+    "sparse_attention_with_repetition",
+    "token_mask_from_blocks",
+]

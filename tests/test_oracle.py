@@ -1,0 +1,353 @@
+"""Pins of the fp64 oracle against things other than itself: hand-derived worked
+examples (tests/golden/hand_examples.json), a library routine (torch's CPU
+scaled_dot_product_attention in fp64, torch.softmax), closed forms, invariants and
+brute force over subsets.  CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    """torch's CPU fp64 SDPA; mask is a bool [N, N] (True = attend)."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, scale=scale)
+    return o[0, 0].numpy()
+
+
+# ---------------------------------------------------------------- dense attention
+
+@pytest.mark.parametrize("n,d,seed", [(7, 4, 0), (64, 16, 1), (100, 32, 2)])
+def test_dense_matches_library_sdpa(n, d, seed):
+    q, k, v = _rand((n, d), seed), _rand((n, d), seed + 10), _rand((n, d), seed + 20)
+    o, lse = oracle.dense_attention(q, k, v)
+    ref = _sdpa(q, k, v, 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    s = torch.from_numpy(q @ k.T / math.sqrt(d))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_dense_closed_forms():
+    n, d = 37, 8
+    v = _rand((n, d), 3)
+    # Q = 0: every logit is 0, the softmax is uniform, o_i = mean_j v_j, LSE = ln N.
+    o, lse = oracle.dense_attention(np.zeros((n, d)), _rand((n, d), 4), v)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(0), o.shape), atol=1e-13)
+    np.testing.assert_allclose(lse, math.log(n), atol=1e-13)
+    # constant V: convex weights reproduce the constant row.
+    c = _rand((1, d), 5)
+    o, _ = oracle.dense_attention(_rand((n, d), 6), _rand((n, d), 7), np.repeat(c, n, 0))
+    np.testing.assert_allclose(o, np.repeat(c, n, 0), atol=1e-13)
+
+
+def test_dense_explicit_scale():
+    q, k, v = _rand((20, 8), 8), _rand((20, 8), 9), _rand((20, 8), 10)
+    o, _ = oracle.dense_attention(q, k, v, scale=0.37)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, 0.37), atol=1e-12)
+
+
+# ---------------------------------------------------------------- hand example
+
+def _hand():
+    g = GOLD["softmax_example"]
+    q = np.array(g["q"])[:, None]
+    k = np.log(np.array(g["k_exp"]))[:, None]
+    v = np.array(g["v"])[:, None]
+    return g, q, k, v
+
+
+def test_hand_example_dense_energy_select_sparse():
+    g, q, k, v = _hand()
+    o, lse = oracle.dense_attention(q, k, v, scale=g["scale"])
+    np.testing.assert_allclose(o[:, 0], g["dense_o"], atol=1e-12)
+    np.testing.assert_allclose(lse, math.log(g["dense_lse_exp"]), atol=1e-12)
+    e = oracle.block_energy(q, k, g["block"], scale=g["scale"])
+    np.testing.assert_allclose(e, g["energy"], atol=1e-12)
+    for tau, key in ((0.5, "keep_tau_0.5"), (0.75, "keep_tau_0.75")):
+        keep = np.array([oracle.select_row(e[r], tau) for r in range(2)])
+        np.testing.assert_array_equal(keep.astype(int), g[key])
+    mask, votes = oracle.select_blocks(e[None, None], 0.5, rho=0.5, force_diag=True)
+    np.testing.assert_array_equal(mask[0], g["mask_tau_0.5_forced_diag"])
+    o, lse = oracle.sparse_attention(q, k, v, np.array(g["sparse_mask"]), g["block"], scale=g["scale"])
+    np.testing.assert_allclose(o[:, 0], g["sparse_o_num"] / g["sparse_o_den"], atol=1e-12)
+    np.testing.assert_allclose(lse, math.log(g["sparse_lse_exp"]), atol=1e-12)
+
+
+def test_hand_selection_cases():
+    for case in GOLD["selection_examples"]["cases"]:
+        keep = oracle.select_row(np.array(case["e"], dtype=np.float64), case["tau"])
+        np.testing.assert_array_equal(keep.astype(int), case["keep"], err_msg=str(case))
+
+
+def test_hand_aggregation_cases():
+    for case in GOLD["aggregation_example"]["cases"]:
+        keep = oracle.aggregate_votes(np.array(case["votes"]), case["n_draws"], case["rho"])
+        np.testing.assert_array_equal(keep.astype(int), case["keep"])
+
+
+def test_hand_csr_case():
+    g = GOLD["csr_example"]
+    row_ptr, col_idx, order = oracle.build_csr(np.array(g["mask"], dtype=np.uint8))
+    np.testing.assert_array_equal(row_ptr, g["row_ptr"])
+    np.testing.assert_array_equal(col_idx, g["col_idx"])
+    np.testing.assert_array_equal(order, g["work_order"])
+
+
+def test_hand_broadcast_case():
+    g = GOLD["broadcast_example"]
+    n = g["n_prefix"] + int(np.prod(g["grid"]))
+    o = np.arange(n, dtype=np.float64)[:, None] * np.ones((1, 3))
+    out = oracle.row_broadcast(o, g["n_prefix"], g["grid"], g["stride"])
+    np.testing.assert_array_equal(out[:, 0], g["source_token"])
+    rows = oracle.computed_rows(n, g["n_prefix"], g["grid"], g["stride"], True)
+    np.testing.assert_array_equal(rows.astype(int), g["computed_rows"])
+
+
+# ---------------------------------------------------------------- block energy
+
+@pytest.mark.parametrize("n,block", [(64, 16), (70, 16), (33, 8)])
+def test_energy_matches_library_softmax_tiles(n, block):
+    d = 8
+    q, k = _rand((n, d), 11), _rand((n, d), 12)
+    e = oracle.block_energy(q, k, block)
+    p = torch.softmax(torch.from_numpy(q @ k.T / math.sqrt(d)), dim=1).numpy()
+    nb = (n + block - 1) // block
+    ref = np.zeros((nb, nb))
+    for i in range(n):  # brute force: visit every probability once
+        for j in range(n):
+            ref[i // block, j // block] += p[i, j]
+    np.testing.assert_allclose(e, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,block", [(64, 16), (70, 16)])
+def test_energy_invariants(n, block):
+    d = 8
+    q, k = _rand((n, d), 13) * 3, _rand((n, d), 14)
+    e = oracle.block_energy(q, k, block)
+    sizes = np.array([min(n, (b + 1) * block) - b * block for b in range((n + block - 1) // block)])
+    assert (e >= 0).all()
+    # each query row's probabilities sum to 1, so a query block's energies sum to its row count
+    np.testing.assert_allclose(e.sum(axis=1), sizes, atol=1e-12)
+    # Q = 0: uniform attention, so E[qb, kb] = |qb| * |kb| / N exactly (up to rounding)
+    e0 = oracle.block_energy(np.zeros((n, d)), k, block)
+    np.testing.assert_allclose(e0, np.outer(sizes, sizes) / n, atol=1e-13)
+
+
+def test_energy_q_blocks_subset():
+    q, k = _rand((50, 8), 15), _rand((50, 8), 16)
+    full = oracle.block_energy(q, k, 16)
+    part = oracle.block_energy(q, k, 16, q_blocks=[3, 0])
+    np.testing.assert_array_equal(part, full[[3, 0]])
+
+
+# ---------------------------------------------------------------- selection
+
+def _brute_force_keep(e, tau):
+    """Smallest subset reaching tau * total; among those, the one whose sorted
+    member list under (energy desc, index asc) is first."""
+    nkb = len(e)
+    total = sum(e)
+    rank = sorted(range(nkb), key=lambda j: (-e[j], j))
+    pos = {j: r for r, j in enumerate(rank)}
+    for size in range(1, nkb + 1):
+        best = None
+        for sub in itertools.combinations(range(nkb), size):
+            if sum(e[j] for j in sub) >= tau * total:
+                key = sorted(pos[j] for j in sub)
+                if best is None or key < best[0]:
+                    best = (key, sub)
+        if best is not None:
+            keep = np.zeros(nkb, dtype=bool)
+            keep[list(best[1])] = True
+            return keep
+    return np.ones(nkb, dtype=bool)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_selection_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    nkb = int(rng.integers(1, 11))
+    e = rng.integers(0, 6, size=nkb).astype(np.float64)  # integers: every partial sum is exact
+    if e.sum() == 0:
+        e[0] = 1.0
+    for tau in (0.1, 0.37, 0.5, 0.8, 0.95, 0.999):
+        keep = oracle.select_row(e, tau)
+        np.testing.assert_array_equal(keep, _brute_force_keep(list(e), tau), err_msg=f"e={e} tau={tau}")
+
+
+def test_selection_monotone_and_extremes():
+    rng = np.random.default_rng(21)
+    e = rng.random(40) ** 4
+    prev = 0
+    for tau in np.linspace(0.01, 0.999, 60):
+        cnt = int(oracle.select_row(e, tau).sum())
+        assert cnt >= prev
+        prev = cnt
+    assert oracle.select_row(e, 1.0).all()
+    tiny = oracle.select_row(e, 1e-9)
+    assert tiny.sum() == 1 and tiny[np.argmax(e)]
+
+
+def test_aggregation_identities():
+    rng = np.random.default_rng(22)
+    e = rng.random((1, 3, 6, 6))
+    # one draw: the aggregated mask is that draw's selection
+    mask, votes = oracle.select_blocks(e, 0.8, rho=0.5, force_diag=False)
+    for h in range(3):
+        for r in range(6):
+            np.testing.assert_array_equal(mask[h, r].astype(bool), oracle.select_row(e[0, h, r], 0.8))
+    # identical draws: same mask, every vote equals the draw count or 0
+    mask4, votes4 = oracle.select_blocks(np.repeat(e, 4, axis=0), 0.8, rho=0.5, force_diag=False)
+    np.testing.assert_array_equal(mask4, mask)
+    assert set(np.unique(votes4)) <= {0, 4}
+
+
+def test_forced_blocks():
+    e = np.zeros((2, 1, 5, 5))
+    e[..., 4] = 1.0  # all energy in the last key block
+    mask, _ = oracle.select_blocks(e, 0.5, rho=0.5, force_diag=True, n_dense_prefix_blocks=2)
+    m = mask[0].astype(bool)
+    assert m[np.arange(5), np.arange(5)].all()
+    assert m[:2, :].all() and m[:, :2].all() and m[:, 4].all()
+    assert not m[2, 3] and not m[3, 2]
+
+
+def test_tau_one_calibration_gives_dense_output():
+    n, d, block = 48, 8, 16
+    q, k, v = _rand((n, d), 23), _rand((n, d), 24), _rand((n, d), 25)
+    e = oracle.block_energy(q, k, block)[None, None]
+    mask, _ = oracle.select_blocks(e, 1.0)
+    assert mask.all()
+    o, lse = oracle.sparse_attention(q, k, v, mask[0], block)
+    od, lsed = oracle.dense_attention(q, k, v)
+    np.testing.assert_allclose(o, od, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, atol=1e-13)
+
+
+# ---------------------------------------------------------------- CSR
+
+@pytest.mark.parametrize("seed", range(4))
+def test_csr_round_trip(seed):
+    rng = np.random.default_rng(seed)
+    rows, nkb = int(rng.integers(1, 50)), int(rng.integers(1, 40))
+    mask = (rng.random((rows, nkb)) < rng.random()).astype(np.uint8)
+    row_ptr, col_idx, order = oracle.build_csr(mask)
+    back = np.zeros_like(mask)
+    for r in range(rows):
+        seg = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        assert (np.diff(seg) > 0).all()
+        back[r, seg] = 1
+    np.testing.assert_array_equal(back, mask)
+    assert row_ptr[-1] == mask.sum()
+    assert sorted(order.tolist()) == list(range(rows))
+    cnt = np.diff(row_ptr)[order]
+    assert (np.diff(cnt) <= 0).all()
+    for a, b in zip(order[:-1], order[1:]):  # equal counts keep row order
+        if cnt[list(order).index(a)] == cnt[list(order).index(b)]:
+            assert a < b
+
+
+# ---------------------------------------------------------------- sparse attention
+
+@pytest.mark.parametrize("n,block,density,seed", [(64, 16, 0.4, 0), (70, 16, 0.5, 1), (96, 32, 0.3, 2)])
+def test_sparse_matches_library_masked_sdpa(n, block, density, seed):
+    d = 8
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand((n, d), 30 + seed), _rand((n, d), 40 + seed), _rand((n, d), 50 + seed)
+    nb = (n + block - 1) // block
+    m = rng.random((nb, nb)) < density
+    np.fill_diagonal(m, True)
+    o, lse = oracle.sparse_attention(q, k, v, m, block)
+    tok = oracle.token_mask_from_blocks(m, block, n)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, 1 / math.sqrt(d), tok), atol=1e-12)
+    s = torch.from_numpy(q @ k.T / math.sqrt(d)).masked_fill(~torch.from_numpy(tok), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, 1).numpy(), atol=1e-12)
+
+
+def test_token_mask_expansion_by_hand():
+    m = np.array([[1, 0], [0, 1]], dtype=bool)
+    t = oracle.token_mask_from_blocks(m, 2, 3)
+    np.testing.assert_array_equal(t, [[1, 1, 0], [1, 1, 0], [0, 0, 1]])
+
+
+def test_sparse_full_mask_is_dense_and_diagonal_is_blockwise():
+    n, d, block = 80, 8, 16
+    q, k, v = _rand((n, d), 60), _rand((n, d), 61), _rand((n, d), 62)
+    nb = n // block
+    o, lse = oracle.sparse_attention(q, k, v, np.ones((nb, nb)), block)
+    od, lsed = oracle.dense_attention(q, k, v)
+    np.testing.assert_allclose(o, od, atol=1e-13)
+    o, _ = oracle.sparse_attention(q, k, v, np.eye(nb), block)
+    for b in range(nb):
+        sl = slice(b * block, (b + 1) * block)
+        np.testing.assert_allclose(o[sl], _sdpa(q[sl], k[sl], v[sl], 1 / math.sqrt(d)), atol=1e-12)
+
+
+def test_sparse_empty_rows_and_row_subset():
+    n, d, block = 48, 4, 16
+    q, k, v = _rand((n, d), 63), _rand((n, d), 64), _rand((n, d), 65)
+    m = np.ones((3, 3), dtype=bool)
+    m[1] = False
+    o, lse = oracle.sparse_attention(q, k, v, m, block)
+    assert (o[16:32] == 0).all() and np.isneginf(lse[16:32]).all()
+    full, _ = oracle.sparse_attention(q, k, v, np.ones((3, 3)), block)
+    rows = np.array([0, 5, 40, 47])
+    part, lp = oracle.sparse_attention(q, k, v, np.ones((3, 3)), block, rows=rows)
+    np.testing.assert_array_equal(part[rows], full[rows])
+    others = np.setdiff1d(np.arange(n), rows)
+    assert (part[others] == 0).all() and np.isneginf(lp[others]).all()
+
+
+# ---------------------------------------------------------------- repetition
+
+def test_broadcast_stride_one_is_identity():
+    o = _rand((2 + 3 * 4 * 5, 6), 70)
+    np.testing.assert_array_equal(oracle.row_broadcast(o, 2, (3, 4, 5), 1), o)
+    assert oracle.computed_rows(o.shape[0], 2, (3, 4, 5), 1, True).all()
+
+
+def test_repetition_equals_full_computation_when_rows_repeat():
+    # Each group of s image rows repeats its anchor row's queries, and the grid is
+    # laid out so a group never straddles a query block (W*s == block): then the
+    # anchors' outputs are exactly every row's output.
+    grid, s, block, n_prefix = (3, 8, 4), 2, 8, 8
+    n = n_prefix + 3 * 8 * 4
+    d = 8
+    rng = np.random.default_rng(71)
+    q = rng.standard_normal((n, d))
+    g = q[n_prefix:].reshape(3, 8, 4, d)
+    g[:, 1::2] = g[:, 0::2]
+    q[n_prefix:] = g.reshape(-1, d)
+    k, v = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    nb = n // block
+    m = rng.random((nb, nb)) < 0.5
+    np.fill_diagonal(m, True)
+    full, lfull = oracle.sparse_attention(q, k, v, m, block)
+    rep, lrep = oracle.sparse_attention_with_repetition(q, k, v, m, block, n_prefix, grid, s, True)
+    np.testing.assert_allclose(rep, full, atol=1e-13)
+    np.testing.assert_allclose(lrep, lfull, atol=1e-13)
+    # a normal head computes every row
+    nrm, _ = oracle.sparse_attention_with_repetition(q, k, v, m, block, n_prefix, grid, s, False)
+    np.testing.assert_array_equal(nrm, full)
+
+
+def test_repetition_short_last_group():
+    # H = 5 with s = 4: anchors 0 and 4; row 4 stands only for itself.
+    rows = oracle.computed_rows(1 * 5 * 3, 0, (1, 5, 3), 4, True)
+    np.testing.assert_array_equal(rows.reshape(5, 3)[:, 0], [1, 0, 0, 0, 1])
+    o = np.arange(15, dtype=np.float64)[:, None]
+    out = oracle.row_broadcast(o, 0, (1, 5, 3), 4).reshape(5, 3)
+    np.testing.assert_array_equal(out[:, 1], [1, 1, 1, 1, 13])
