@@ -1,0 +1,34 @@
+"""Calibrated block-sparse spatiotemporal attention on AMD MI355X (gfx950).
+
+Python binding of libcalibattn.so (C ABI in include/calibattn.h).  The library is
+loaded on first use; a missing library raises instead of falling back.
+"""
+from .api import (
+    CalibAttnError,
+    build_block_csr,
+    calib_block_energy,
+    dense_attn_fwd,
+    make_desc,
+    n_blocks,
+    rep_row_broadcast,
+    select_blocks_by_energy,
+    sparse_attn_fwd,
+    version,
+)
+from ._lib import LIB_PATH, LibraryMissing, load as load_library
+
+__all__ = [
+    "CalibAttnError",
+    "LibraryMissing",
+    "LIB_PATH",
+    "build_block_csr",
+    "calib_block_energy",
+    "dense_attn_fwd",
+    "load_library",
+    "make_desc",
+    "n_blocks",
+    "rep_row_broadcast",
+    "select_blocks_by_energy",
+    "sparse_attn_fwd",
+    "version",
+]

@@ -1,0 +1,72 @@
+"""ctypes loader for libcalibattn.so (built in-tree by build.py).
+
+The library is required: if it is missing or cannot be loaded, every call raises.
+There is no fallback implementation.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("CALIBATTN_LIB", os.path.join(_PKG, "libcalibattn.so"))
+
+# Every symbol the header include/calibattn.h declares, with its C signature.
+c_i32, c_i64, c_f32, c_f64, c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", c_i32),
+        ("batch", c_i32),
+        ("heads", c_i32),
+        ("seq_len", c_i32),
+        ("head_dim", c_i32),
+        ("block", c_i32),
+        ("n_prefix", c_i32),
+        ("grid_f", c_i32),
+        ("grid_h", c_i32),
+        ("grid_w", c_i32),
+        ("scale", c_f32),
+        ("stride_b", c_i64),
+        ("stride_h", c_i64),
+        ("stride_n", c_i64),
+    ]
+
+
+_PD = ctypes.POINTER(AttnDesc)
+SIGNATURES = {
+    "calib_block_energy": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
+    "select_blocks_by_energy": (c_i32, [c_p, c_i32, c_i32, c_i32, c_f64, c_f64, c_i32, c_i32, c_p, c_p, c_p]),
+    "build_block_csr": (c_i32, [c_p, c_i32, c_i32, c_p, c_p, c_i64, c_p, c_p]),
+    "sparse_attn_fwd": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p, c_i32, c_i32, c_p, c_p, c_p]),
+    "rep_row_broadcast": (c_i32, [_PD, c_p, c_p, c_i32, c_p]),
+    "dense_attn_fwd": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p, c_p]),
+    "cba_status_str": (ctypes.c_char_p, [c_i32]),
+    "cba_version": (c_i32, []),
+}
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load():
+    """Load (once) and return the library handle; raises LibraryMissing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} not found: build it with `python -m calibrated_block_sparse_calib_amd.build`"
+        )
+    try:
+        lib = ctypes.CDLL(LIB_PATH)
+    except OSError as e:  # pragma: no cover - depends on the ROCm install
+        raise LibraryMissing(f"cannot load {LIB_PATH}: {e}") from e
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,208 @@
+"""Python binding of libcalibattn.so: one function per C entry point, same names.
+
+Argument marshalling only -- every step runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  Attention tensors are
+[batch, heads, seq_len, head_dim] (head_dim contiguous) in float32 or bfloat16 on
+the GPU; q, k, v and o must share one stride pattern.
+"""
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class CalibAttnError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = _lib.load().cba_status_str(status).decode()
+        raise CalibAttnError(f"{what} failed: status {status} ({msg})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise CalibAttnError("tensors must be on the GPU")
+
+
+def make_desc(q: torch.Tensor, block: int, n_prefix: int = 0, grid: Optional[Sequence[int]] = None,
+              scale: float = 0.0) -> _lib.AttnDesc:
+    """Descriptor of a [batch, heads, seq_len, head_dim] attention problem."""
+    if q.dim() != 4:
+        raise CalibAttnError("expected a [batch, heads, seq_len, head_dim] tensor")
+    if q.dtype not in _DTYPES:
+        raise CalibAttnError(f"unsupported dtype {q.dtype}")
+    if q.stride(3) != 1:
+        raise CalibAttnError("head_dim must be contiguous")
+    b, h, n, d = q.shape
+    gf, gh, gw = (0, 0, 0) if grid is None else (int(x) for x in grid)
+    return _lib.AttnDesc(
+        _DTYPES[q.dtype], b, h, n, d, int(block), int(n_prefix), gf, gh, gw, float(scale),
+        q.stride(0), q.stride(1), q.stride(2),
+    )
+
+
+def _same_layout(ref: torch.Tensor, *ts):
+    for t in ts:
+        if t is None:
+            continue
+        if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
+            raise CalibAttnError("q, k, v and o must share shape, strides and dtype")
+
+
+def _rep_array(rep_heads, heads):
+    if rep_heads is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(rep_heads, dtype=np.uint8).reshape(-1))
+    if arr.shape[0] != heads:
+        raise CalibAttnError("rep_heads needs one flag per head")
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def n_blocks(seq_len: int, block: int) -> int:
+    return (seq_len + block - 1) // block
+
+
+def calib_block_energy(q, k, v=None, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,
+                       lse: Optional[torch.Tensor] = None, energy: Optional[torch.Tensor] = None,
+                       o: Optional[torch.Tensor] = None):
+    """Dense pass (LSE cached, O when v is given) then block energies.
+    The batch index is the calibration draw.  Returns (energy, lse, o)."""
+    _require_gpu(q, k, v)
+    _same_layout(q, k, v)
+    desc = make_desc(q, block, n_prefix, grid, scale)
+    b, h, n, _ = q.shape
+    nb = n_blocks(n, block)
+    if lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if energy is None:
+        energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
+    if v is not None and o is None:
+        o = torch.empty_like(q)
+    if not (lse.is_contiguous() and energy.is_contiguous()):
+        raise CalibAttnError("lse and energy must be contiguous")
+    _check(_lib.load().calib_block_energy(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                          _ptr(lse), _ptr(energy), _stream()), "calib_block_energy")
+    return energy, lse, o
+
+
+def select_blocks_by_energy(energy: torch.Tensor, tau: float, rho: float = 0.5, force_diag: bool = True,
+                            n_dense_prefix_blocks: int = 0, mask: Optional[torch.Tensor] = None,
+                            votes: Optional[torch.Tensor] = None, return_votes: bool = False):
+    """energy: fp32 [draws, heads, nb, nb] -> mask uint8 [heads, nb, nb] (and votes)."""
+    _require_gpu(energy)
+    if energy.dtype != torch.float32 or energy.dim() != 4 or not energy.is_contiguous():
+        raise CalibAttnError("energy must be contiguous fp32 [draws, heads, nb, nb]")
+    d, h, nb, nb2 = energy.shape
+    if nb != nb2:
+        raise CalibAttnError("energy must be square per head")
+    if mask is None:
+        mask = torch.empty((h, nb, nb), dtype=torch.uint8, device=energy.device)
+    if return_votes and votes is None:
+        votes = torch.empty((h, nb, nb), dtype=torch.int32, device=energy.device)
+    _check(_lib.load().select_blocks_by_energy(_ptr(energy), d, h, nb, float(tau), float(rho), int(bool(force_diag)),
+                                               int(n_dense_prefix_blocks), _ptr(mask), _ptr(votes), _stream()),
+           "select_blocks_by_energy")
+    return (mask, votes) if return_votes else mask
+
+
+def build_block_csr(mask: torch.Tensor, with_order: bool = True, exact: bool = False,
+                    ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """mask uint8 [..., nkb] (rows = all leading dims) -> (row_ptr, col_idx, work_order).
+
+    exact=False: one call with capacity rows * nkb (no host synchronisation); the
+    first row_ptr[-1] entries of col_idx are the skip list.  exact=True: a count
+    pass, a host read of nnz, then the fill into a tensor of exactly nnz entries."""
+    _require_gpu(mask)
+    if mask.dtype != torch.uint8 or not mask.is_contiguous():
+        raise CalibAttnError("mask must be contiguous uint8")
+    nkb = mask.shape[-1]
+    rows = mask.numel() // nkb
+    lib = _lib.load()
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=mask.device)
+    order = torch.empty(rows, dtype=torch.int32, device=mask.device) if with_order else None
+    if exact:
+        _check(lib.build_block_csr(_ptr(mask), rows, nkb, _ptr(row_ptr), None, 0, None, _stream()),
+               "build_block_csr(count)")
+        cap = int(row_ptr[-1].item())
+    else:
+        cap = rows * nkb
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=mask.device)
+    _check(lib.build_block_csr(_ptr(mask), rows, nkb, _ptr(row_ptr), _ptr(col_idx), cap, _ptr(order), _stream()),
+           "build_block_csr")
+    return row_ptr, col_idx, order
+
+
+def sparse_attn_fwd(q, k, v, row_ptr, col_idx, *, block: int, work_order=None, rep_heads=None,
+                    anchor_stride: int = 1, fuse_broadcast: bool = True, n_prefix: int = 0, grid=None,
+                    scale: float = 0.0, o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    return_lse: bool = False):
+    """Block-sparse attention over the kept blocks in (row_ptr, col_idx)."""
+    _require_gpu(q, k, v, row_ptr, col_idx, work_order, o, lse)
+    if o is None:
+        o = torch.empty_like(q)
+    _same_layout(q, k, v, o)
+    desc = make_desc(q, block, n_prefix, grid, scale)
+    b, h, n, _ = q.shape
+    if return_lse and lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise CalibAttnError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != h * n_blocks(n, block) + 1:
+        raise CalibAttnError("row_ptr must have heads * nb + 1 entries")
+    if work_order is not None and (work_order.dtype != torch.int32 or work_order.numel() != h * n_blocks(n, block)):
+        raise CalibAttnError("work_order must be int32 [heads * nb]")
+    rep_arr, rep_ptr = _rep_array(rep_heads, h)
+    _check(_lib.load().sparse_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
+                                       col_idx.numel(), _ptr(work_order), rep_ptr, int(anchor_stride),
+                                       int(bool(fuse_broadcast)), _ptr(o), _ptr(lse), _stream()),
+           "sparse_attn_fwd")
+    del rep_arr
+    return (o, lse) if return_lse else o
+
+
+def rep_row_broadcast(o: torch.Tensor, rep_heads, anchor_stride: int, *, block: int, n_prefix: int = 0,
+                      grid=None):
+    """Copy anchor-row outputs to their follower rows, in place.  Returns o."""
+    _require_gpu(o)
+    desc = make_desc(o, block, n_prefix, grid)
+    rep_arr, rep_ptr = _rep_array(rep_heads, o.shape[1])
+    _check(_lib.load().rep_row_broadcast(ctypes.byref(desc), _ptr(o), rep_ptr, int(anchor_stride), _stream()),
+           "rep_row_broadcast")
+    del rep_arr
+    return o
+
+
+def dense_attn_fwd(q, k, v, *, block: int = 128, scale: float = 0.0, o: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Dense attention over every key (the baseline)."""
+    _require_gpu(q, k, v, o, lse)
+    if o is None:
+        o = torch.empty_like(q)
+    _same_layout(q, k, v, o)
+    desc = make_desc(q, block, 0, None, scale)
+    b, h, n, _ = q.shape
+    if return_lse and lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    _check(_lib.load().dense_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream()),
+           "dense_attn_fwd")
+    return (o, lse) if return_lse else o
+
+
+def version() -> int:
+    return int(_lib.load().cba_version())

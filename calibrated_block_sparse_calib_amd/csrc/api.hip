@@ -1,0 +1,202 @@
+// C ABI of libcalibattn.so: argument validation on the host and dispatch to the
+// kernels.  Every entry point either returns an error before enqueuing anything or
+// enqueues its kernels on the caller's stream and returns without waiting.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/calibattn.h"
+#include "cba_internal.h"
+
+#define CBA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using cba::AttnParams;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == CBA_DTYPE_BF16 ? 2 : 4; }
+
+// Shape, stride and dtype checks shared by every attention-shaped call.
+cba_status check_desc(const cba_attn_desc* d) {
+  if (!d) return CBA_EINVAL;
+  if (d->dtype != CBA_DTYPE_F32 && d->dtype != CBA_DTYPE_BF16) return CBA_EUNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return CBA_EUNSUPPORTED;
+  if (d->block != 32 && d->block != 64 && d->block != 128) return CBA_EUNSUPPORTED;
+  if (d->batch < 1 || d->heads < 1 || d->seq_len < 1) return CBA_EINVAL;
+  if (d->n_prefix < 0 || d->n_prefix > d->seq_len || d->n_prefix % d->block != 0) return CBA_EINVAL;
+  if (d->grid_f < 0 || d->grid_h < 0 || d->grid_w < 0) return CBA_EINVAL;
+  const int64_t grid = (int64_t)d->grid_f * d->grid_h * d->grid_w;
+  if (grid != 0 && grid != (int64_t)d->seq_len - d->n_prefix) return CBA_EINVAL;
+  if (!std::isfinite(d->scale)) return CBA_EINVAL;
+  if (d->stride_n < d->head_dim || d->stride_h < 0 || d->stride_b < 0) return CBA_EINVAL;
+  const int eb = elem_bytes(d->dtype);
+  if ((d->stride_n * eb) % 16 || (d->stride_h * eb) % 16 || (d->stride_b * eb) % 16) return CBA_EINVAL;
+  const int64_t nb = ((int64_t)d->seq_len + d->block - 1) / d->block;
+  if ((int64_t)d->heads * nb * d->batch > INT32_MAX) return CBA_EINVAL;
+  if ((int64_t)d->batch * d->heads > 65535) return CBA_EINVAL;
+  return CBA_OK;
+}
+
+cba_status check_tensor(const void* p) { return (p && aligned16(p)) ? CBA_OK : CBA_EINVAL; }
+
+AttnParams make_params(const cba_attn_desc* d) {
+  AttnParams p{};
+  p.batch = d->batch;
+  p.heads = d->heads;
+  p.n = d->seq_len;
+  p.nb = (d->seq_len + d->block - 1) / d->block;
+  p.n_rows = d->heads * p.nb;
+  p.n_prefix = d->n_prefix;
+  p.gf = d->grid_f;
+  p.gh = d->grid_h;
+  p.gw = d->grid_w;
+  p.sb = d->stride_b;
+  p.sh = d->stride_h;
+  p.sn = d->stride_n;
+  const float scale = d->scale == 0.f ? 1.0f / std::sqrt((float)d->head_dim) : d->scale;
+  p.c = scale * cba::kLog2e;
+  p.anchor_stride = 1;
+  return p;
+}
+
+// Packs the host repetition flags; fails when repetition is asked for without a
+// token grid or beyond the supported head count.
+cba_status set_rep(AttnParams& p, const cba_attn_desc* d, const uint8_t* rep_heads, int32_t anchor_stride) {
+  if (anchor_stride < 1) return CBA_EINVAL;
+  p.anchor_stride = anchor_stride;
+  if (!rep_heads) return CBA_OK;
+  bool any = false;
+  for (int h = 0; h < d->heads; ++h) any |= rep_heads[h] != 0;
+  if (!any) return CBA_OK;
+  if (d->heads > cba::kMaxRepHeads) return CBA_EINVAL;
+  if ((int64_t)d->grid_f * d->grid_h * d->grid_w == 0) return CBA_EINVAL;
+  for (int h = 0; h < d->heads; ++h)
+    if (rep_heads[h]) p.rep_bits[h >> 5] |= 1u << (h & 31);
+  p.has_rep = 1;
+  return CBA_OK;
+}
+
+cba_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return CBA_OK;
+  (void)hipGetLastError();  // clear the sticky launch error for the caller
+  return CBA_EHIP;
+}
+
+// Dense when p.row_ptr is null.
+hipError_t run_attention(const AttnParams& p, const cba_attn_desc* d, bool with_pv, hipStream_t s) {
+  return d->dtype == CBA_DTYPE_BF16 ? cba::launch_attn_bf16(p, d->head_dim, d->block, with_pv, s)
+                                    : cba::launch_attn_f32(p, d->head_dim, d->block, with_pv, s);
+}
+
+}  // namespace
+
+CBA_API cba_status calib_block_energy(const cba_attn_desc* desc, const void* q, const void* k, const void* v,
+                                      void* o, float* lse, float* energy, cba_stream_t stream) {
+  cba_status st = check_desc(desc);
+  if (st) return st;
+  if (check_tensor(q) || check_tensor(k) || !lse || !energy) return CBA_EINVAL;
+  if ((v == nullptr) != (o == nullptr)) return CBA_EINVAL;
+  if (v && (check_tensor(v) || check_tensor(o))) return CBA_EINVAL;
+  AttnParams p = make_params(desc);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.energy = energy;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // Sweep 1: dense pass, caches LSE (and writes O when V is given).
+  hipError_t e = run_attention(p, desc, /*with_pv=*/v != nullptr, s);
+  if (e != hipSuccess) return from_hip(e);
+  // Sweep 2: tile sums of exp(s - lse).
+  e = desc->dtype == CBA_DTYPE_BF16 ? cba::launch_energy_bf16(p, desc->head_dim, desc->block, s)
+                                    : cba::launch_energy_f32(p, desc->head_dim, desc->block, s);
+  return from_hip(e);
+}
+
+CBA_API cba_status select_blocks_by_energy(const float* energy, int32_t n_draws, int32_t heads, int32_t nb,
+                                           double tau, double rho, int32_t force_diag,
+                                           int32_t n_dense_prefix_blocks, uint8_t* mask, int32_t* votes,
+                                           cba_stream_t stream) {
+  if (!energy || !mask) return CBA_EINVAL;
+  if (n_draws < 1 || heads < 1 || nb < 1 || nb > 4096) return CBA_EINVAL;
+  if ((int64_t)heads * nb > INT32_MAX) return CBA_EINVAL;
+  if (!std::isfinite(tau) || !std::isfinite(rho) || tau < 0.0) return CBA_EINVAL;
+  if (n_dense_prefix_blocks < 0 || n_dense_prefix_blocks > nb) return CBA_EINVAL;
+  return from_hip(cba::launch_select(energy, n_draws, heads, nb, tau, rho, force_diag != 0, n_dense_prefix_blocks,
+                                     mask, votes, reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status build_block_csr(const uint8_t* mask, int32_t n_rows, int32_t nkb, int32_t* row_ptr,
+                                   int32_t* col_idx, int64_t col_idx_capacity, int32_t* work_order,
+                                   cba_stream_t stream) {
+  if (!mask || !row_ptr || n_rows < 1 || nkb < 1) return CBA_EINVAL;
+  if ((int64_t)n_rows * nkb > INT32_MAX) return CBA_EINVAL;  // nnz must fit int32
+  if (col_idx && col_idx_capacity < 0) return CBA_EINVAL;
+  return from_hip(cba::launch_csr(mask, n_rows, nkb, row_ptr, col_idx, col_idx ? col_idx_capacity : 0, work_order,
+                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status sparse_attn_fwd(const cba_attn_desc* desc, const void* q, const void* k, const void* v,
+                                   const int32_t* row_ptr, const int32_t* col_idx, int64_t col_idx_len,
+                                   const int32_t* work_order, const uint8_t* rep_heads, int32_t anchor_stride,
+                                   int32_t fuse_broadcast, void* o, float* lse, cba_stream_t stream) {
+  cba_status st = check_desc(desc);
+  if (st) return st;
+  if (check_tensor(q) || check_tensor(k) || check_tensor(v) || check_tensor(o)) return CBA_EINVAL;
+  if (!row_ptr || col_idx_len < 0 || (col_idx_len > 0 && !col_idx)) return CBA_EINVAL;
+  AttnParams p = make_params(desc);
+  if ((st = set_rep(p, desc, rep_heads, anchor_stride))) return st;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
+  p.col_len = col_idx_len;
+  p.work_order = work_order;
+  p.fuse_broadcast = fuse_broadcast != 0;
+  return from_hip(run_attention(p, desc, /*with_pv=*/true, reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status rep_row_broadcast(const cba_attn_desc* desc, void* o, const uint8_t* rep_heads,
+                                     int32_t anchor_stride, cba_stream_t stream) {
+  cba_status st = check_desc(desc);
+  if (st) return st;
+  if (check_tensor(o) || !rep_heads) return CBA_EINVAL;
+  AttnParams p = make_params(desc);
+  if ((st = set_rep(p, desc, rep_heads, anchor_stride))) return st;
+  p.o = o;
+  if (!p.has_rep || anchor_stride == 1) return CBA_OK;  // nothing to copy
+  return from_hip(
+      cba::launch_broadcast(p, desc->head_dim, elem_bytes(desc->dtype), reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status dense_attn_fwd(const cba_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
+                                  float* lse, cba_stream_t stream) {
+  cba_status st = check_desc(desc);
+  if (st) return st;
+  if (check_tensor(q) || check_tensor(k) || check_tensor(v) || check_tensor(o)) return CBA_EINVAL;
+  AttnParams p = make_params(desc);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  return from_hip(run_attention(p, desc, /*with_pv=*/true, reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API const char* cba_status_str(cba_status status) {
+  switch (status) {
+    case CBA_OK: return "ok";
+    case CBA_EINVAL: return "invalid argument";
+    case CBA_EUNSUPPORTED: return "unsupported dtype, head_dim or block";
+    case CBA_EHIP: return "HIP launch failed";
+    case CBA_ECAPACITY: return "buffer too small";
+    default: return "unknown status";
+  }
+}
+
+CBA_API int32_t cba_version(void) { return 100; }

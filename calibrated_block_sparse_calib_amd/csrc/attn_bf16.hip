@@ -1,0 +1,497 @@
+// bf16 attention kernels for gfx950: block-sparse / dense forward and the
+// block-energy sweep.  bf16 operands on the matrix cores (v_mfma_f32_32x32x16_bf16),
+// fp32 accumulation and fp32 online softmax.
+//
+// Work decomposition: one workgroup per (query block, batch item) -- B query
+// rows -- with B/32 waves of 32 query rows each.  The workgroup walks the key
+// blocks listed for its query block (the skip list of the CalibAtt inference
+// stage, zh S2.2B / fr S2C) in steps of KT keys.  Each step stages a K tile and a
+// V tile in LDS (double buffered, one barrier per step, the next step's global
+// loads in flight during the current step's math).
+//
+// Per wave and step the scores are computed transposed, S^T = K Q^T, so that
+// every lane owns one query row: the row max and row sum of the online softmax
+// stay in-lane except for one exchange between the two 32-lane halves.  The
+// probabilities are kept in the MFMA accumulator layout and fed straight back as
+// the B operand of O^T += V^T P^T; V^T fragments come from the row-major V tile
+// through the LDS transpose read (ds_read_b64_tr_b16), with the key order of
+// each fragment matched to the order in which the accumulator holds P.
+//
+// The running maximum is rescaled lazily: the output and sum are rescaled only
+// when a row maximum grows by more than 2^8 in base-2 units, so most steps skip
+// the rescale.  Numerator and denominator always share the same reference, so
+// the result is the exact softmax up to rounding.
+#include "cba_internal.h"
+
+namespace cba {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t bfraw;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLazyRescale = 8.0f;
+
+template <int D, int B>
+struct Cfg {
+  static constexpr int NW = B / 32;              // waves, 32 query rows each
+  static constexpr int NT = NW * 64;             // threads
+  static constexpr int KT = B < 64 ? B : 64;     // keys per step
+  static constexpr int SPB = B / KT;             // steps per key block
+  static constexpr int RS = D + 16;              // LDS row stride (elements): 32-byte pad
+  static constexpr int TILE = KT * RS;           // elements in one K or V tile
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int CPT = KT * CPR / NT;      // chunks per thread per tile
+  static constexpr int KS = D / 16;              // k-steps of the QK^T product
+  static constexpr int DT = D / 32;              // 32-wide d tiles of O
+  static constexpr int ST = KT / 32;             // 32-key score tiles per step
+  static_assert(KT * CPR % NT == 0, "tile chunks must divide evenly");
+};
+
+// Value held by lane (l ^ 32).
+__device__ inline float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// p points into LDS: the explicit address-space casts make the compiler emit
+// ds_read instructions rather than flat loads.
+__device__ inline bf16x8 lds_read8(const bfraw* p) {
+  return *(const LDS_AS bf16x8*)(p);
+}
+
+__device__ inline i16x4 lds_read_tr(const bfraw* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p));
+}
+
+// Token rows of query block qb that this workgroup computes.  Normal heads: all
+// rows.  Repetition heads: text rows and the anchor image rows (y % stride == 0).
+// Writes the compacted in-block offsets to rowlist and returns their count.
+template <int B, int NT>
+__device__ int build_rowlist(const AttnParams& p, int q0, bool rep, int* rowlist, int* wcnt) {
+  if (!rep) return min(B, p.n - q0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bool flag = false;
+  if (tid < B) {
+    const int tok = q0 + tid;
+    if (tok < p.n) {
+      if (tok < p.n_prefix) {
+        flag = true;
+      } else {
+        const int y = ((tok - p.n_prefix) / p.gw) % p.gh;
+        flag = (y % p.anchor_stride) == 0;
+      }
+    }
+  }
+  const uint64_t bal = __ballot(flag);
+  const int before = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) wcnt[wave] = __popcll(bal);
+  __syncthreads();
+  int off = 0, total = 0;
+  for (int w = 0; w < NT / 64; ++w) {
+    off += (w < wave) ? wcnt[w] : 0;
+    total += wcnt[w];
+  }
+  if (flag) rowlist[off + before] = tid;
+  __syncthreads();
+  return total;
+}
+
+// PV: compute O (otherwise only the log-sum-exp, for the energy sweep).
+// LSE: keep the exact fp32 row sum for the log-sum-exp output.
+// O is normalised by the sum of the same bf16-rounded weights that multiply V, so
+// rounding the weights perturbs a convex combination instead of scaling it.
+template <int D, int B, bool PV, bool LSE>
+__global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParams p) {
+  using C = Cfg<D, B>;
+  extern __shared__ __attribute__((aligned(16))) bfraw lds[];
+  __shared__ int rowlist[B];
+  __shared__ int wcnt[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+  const int item = blockIdx.x;
+  const int it = item / p.batch, b = item - it * p.batch;
+  const int row = p.work_order ? p.work_order[it] : it;
+  if (row < 0 || row >= p.n_rows) return;
+  const int h = row / p.nb, qb = row - h * p.nb;
+  const int q0 = qb * B;
+  const bool rep = rep_head(p, h);
+  const int M = build_rowlist<B, C::NT>(p, q0, rep, rowlist, wcnt);
+
+  const int64_t head_off = (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const bfraw* qg = static_cast<const bfraw*>(p.q) + head_off;
+  const bfraw* kg = static_cast<const bfraw*>(p.k) + head_off;
+  const bfraw* vg = PV ? static_cast<const bfraw*>(p.v) + head_off : nullptr;
+
+  // This lane's query row (the column of the transposed score tile).
+  const int qi = wave * 32 + (lane & 31);
+  const bool wave_active = wave * 32 < M;
+  const bool q_valid = qi < M;
+  const int qtok = q0 + (rep ? (q_valid ? rowlist[qi] : 0) : qi);
+
+  bf16x8 qf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    if (q_valid) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qtok * p.sn + ks * 16 + g * 8);
+    } else {
+      qf[ks] = bf16x8{};
+    }
+  }
+
+  // Key-block list of this row (no list: every key block, in order).
+  const bool dense = p.row_ptr == nullptr;
+  int beg = 0, nblk = p.nb;
+  if (!dense) {
+    beg = max(p.row_ptr[row], 0);
+    const int64_t end = min((int64_t)p.row_ptr[row + 1], p.col_len);
+    nblk = (int)max((int64_t)0, end - beg);
+  }
+  const int nsteps = nblk * C::SPB;
+  auto step_key0 = [&](int s) -> int {
+    const int kb = dense ? s / C::SPB : p.col_idx[beg + s / C::SPB];
+    if (kb < 0 || kb >= p.nb) return -1;
+    const int k0 = kb * B + (s % C::SPB) * C::KT;
+    return k0 < p.n ? k0 : -1;
+  };
+
+  uint4 kreg[C::CPT], vreg[PV ? C::CPT : 1];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < C::CPT; ++c) {
+      const int idx = tid + c * C::NT;
+      const int r = idx / C::CPR, col = idx - r * C::CPR;
+      const int key = k0 + r;
+      if (k0 >= 0 && key < p.n) {
+        kreg[c] = *reinterpret_cast<const uint4*>(kg + (int64_t)key * p.sn + col * 8);
+        if (PV) vreg[c] = *reinterpret_cast<const uint4*>(vg + (int64_t)key * p.sn + col * 8);
+      } else {
+        kreg[c] = make_uint4(0, 0, 0, 0);
+        if (PV) vreg[c] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    bfraw* kt = lds + buf * C::TILE;
+    bfraw* vt = lds + (2 + buf) * C::TILE;
+#pragma unroll
+    for (int c = 0; c < C::CPT; ++c) {
+      const int idx = tid + c * C::NT;
+      const int r = idx / C::CPR, col = idx - r * C::CPR;
+      *reinterpret_cast<uint4*>(kt + r * C::RS + col * 8) = kreg[c];
+      if (PV) *reinterpret_cast<uint4*>(vt + r * C::RS + col * 8) = vreg[c];
+    }
+  };
+
+  f32x16 oacc[PV ? C::DT : 1];
+#pragma unroll
+  for (int dt = 0; dt < (PV ? C::DT : 1); ++dt) oacc[dt] = f32x16{};
+  float m_used = -INFINITY;  // reference maximum, base-2 units
+  float l_part = 0.f;        // this lane's share of the exact row sum (LSE)
+  float r_part = 0.f;        // this lane's share of the rounded-weight sum (O)
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  int k0_cur = nsteps > 0 ? step_key0(0) : -1;
+  if (nsteps > 0) gload(k0_cur);
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    lstore(buf);
+    __syncthreads();
+    int k0_next = -1;
+    if (s + 1 < nsteps) {
+      k0_next = step_key0(s + 1);
+      gload(k0_next);
+    }
+    if (wave_active && k0_cur >= 0) {
+      const bfraw* kt = lds + buf * C::TILE;
+      const bfraw* vt = lds + (2 + buf) * C::TILE;
+      f32x16 sacc[C::ST];
+#pragma unroll
+      for (int t = 0; t < C::ST; ++t) {
+        sacc[t] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8 a = lds_read8(kt + (t * 32 + (lane & 31)) * C::RS + ks * 16 + g * 8);
+          sacc[t] = mfma(a, qf[ks], sacc[t]);
+        }
+      }
+      // Keys past the end of the sequence (ragged last block) take no part.
+      if (k0_cur + C::KT > p.n) {
+#pragma unroll
+        for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0_cur + t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+            if (key >= p.n) sacc[t][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[t][i]);
+      mx = fmaxf(mx, other_half(mx));
+      const float mt = mx * p.c;
+      if (__ballot(mt > m_used + kLazyRescale)) {
+        const float m_new = fmaxf(m_used, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+        l_part *= alpha;
+        r_part *= alpha;
+        if (PV) {
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        }
+        m_used = m_new;
+      }
+      bf16x8 pb[C::ST][2];
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][k2 * 8 + e], p.c, -m_used));
+            if (LSE || !PV) ps += x;
+            if (PV) pb[t][k2][e] = (__bf16)x;
+          }
+      l_part += ps;
+      if (PV) {
+#pragma unroll
+        for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2 pair = {pb[t][k2][e], pb[t][k2][e + 1]};
+              r_part = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, r_part, false);
+            }
+        const int G = lane >> 4, li = lane & 15;
+#pragma unroll
+        for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int krow = t * 32 + k2 * 16 + 4 * g + (li >> 2);
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+              const int dcol = dt * 32 + (G & 1) * 16 + 4 * (li & 3);
+              const i16x4 lo = lds_read_tr(vt + krow * C::RS + dcol);
+              const i16x4 hi = lds_read_tr(vt + (krow + 8) * C::RS + dcol);
+              const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              oacc[dt] = mfma(va, pb[t][k2], oacc[dt]);
+            }
+          }
+      }
+    }
+    k0_cur = k0_next;
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_part + other_half(l_part);
+  const float r_tot = r_part + other_half(r_part);
+  if (!q_valid) return;
+  const float inv = r_tot > 0.f ? 1.f / r_tot : 0.f;
+  const float lse_val = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
+
+  // Repetition heads: the anchor stands for the next stride-1 image rows of its frame.
+  int n_follow = 0;
+  if (rep && qtok >= p.n_prefix) {
+    const int y = ((qtok - p.n_prefix) / p.gw) % p.gh;
+    n_follow = min(p.anchor_stride - 1, p.gh - 1 - y);
+  }
+
+  if (PV && p.o) {
+    bfraw* og = static_cast<bfraw*>(p.o) + head_off;
+    const int n_copies = p.fuse_broadcast ? n_follow : 0;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[dt][r * 4 + e] * inv);
+        const int d = dt * 32 + r * 8 + g * 4;
+        for (int cp = 0; cp <= n_copies; ++cp) {
+          *reinterpret_cast<bf16x4*>(og + (int64_t)(qtok + cp * p.gw) * p.sn + d) = w;
+        }
+      }
+  }
+  if ((LSE || !PV) && p.lse && g == 0) {
+    float* lg = p.lse + ((int64_t)b * p.heads + h) * p.n;
+    for (int cp = 0; cp <= n_follow; ++cp) lg[qtok + cp * p.gw] = lse_val;
+  }
+}
+
+// Block energy, sweep 2: E[qb, kb] = sum over the tile of exp(s_ij - lse_i), with
+// lse cached by the dense sweep.  One workgroup per (query block, batch item); each
+// wave sums its 32 rows' probabilities per key block in-lane, reduces across the
+// wave, and the per-wave partials are added in wave order at the end, so the
+// result is deterministic.
+template <int D, int B>
+__global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnParams p) {
+  using C = Cfg<D, B>;
+  extern __shared__ __attribute__((aligned(16))) bfraw lds[];
+  float* part = reinterpret_cast<float*>(lds + 2 * C::TILE);  // [NW][nb]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+  const int item = blockIdx.x;
+  const int it = item / p.batch, b = item - it * p.batch;
+  const int h = it / p.nb, qb = it - h * p.nb;
+  const int q0 = qb * B;
+  const int M = min(B, p.n - q0);
+
+  const int64_t head_off = (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const bfraw* qg = static_cast<const bfraw*>(p.q) + head_off;
+  const bfraw* kg = static_cast<const bfraw*>(p.k) + head_off;
+  const int qi = wave * 32 + (lane & 31);
+  const bool wave_active = wave * 32 < M;
+  const bool q_valid = qi < M;
+  const int qtok = q0 + qi;
+
+  bf16x8 qf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    qf[ks] = q_valid ? *reinterpret_cast<const bf16x8*>(qg + (int64_t)qtok * p.sn + ks * 16 + g * 8)
+                     : bf16x8{};
+  }
+  // exp2(s*c - lse2) with lse2 = +inf gives 0: rows past the end add nothing.
+  const float lse2 = q_valid ? p.lse[((int64_t)b * p.heads + h) * p.n + qtok] * kLog2e : INFINITY;
+
+  const int nsteps = p.nb * C::SPB;
+  auto step_key0 = [&](int s) -> int {
+    const int k0 = (s / C::SPB) * B + (s % C::SPB) * C::KT;
+    return k0 < p.n ? k0 : -1;
+  };
+  uint4 kreg[C::CPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < C::CPT; ++c) {
+      const int idx = tid + c * C::NT;
+      const int r = idx / C::CPR, col = idx - r * C::CPR;
+      const int key = k0 + r;
+      kreg[c] = (k0 >= 0 && key < p.n)
+                    ? *reinterpret_cast<const uint4*>(kg + (int64_t)key * p.sn + col * 8)
+                    : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  float esum = 0.f;
+  int k0_cur = step_key0(0);
+  gload(k0_cur);
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    bfraw* kt = lds + buf * C::TILE;
+#pragma unroll
+    for (int c = 0; c < C::CPT; ++c) {
+      const int idx = tid + c * C::NT;
+      const int r = idx / C::CPR, col = idx - r * C::CPR;
+      *reinterpret_cast<uint4*>(kt + r * C::RS + col * 8) = kreg[c];
+    }
+    __syncthreads();
+    int k0_next = -1;
+    if (s + 1 < nsteps) {
+      k0_next = step_key0(s + 1);
+      gload(k0_next);
+    }
+    if (wave_active && k0_cur >= 0) {
+#pragma unroll
+      for (int t = 0; t < C::ST; ++t) {
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8 a = lds_read8(kt + (t * 32 + (lane & 31)) * C::RS + ks * 16 + g * 8);
+          sacc = mfma(a, qf[ks], sacc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0_cur + t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], p.c, -lse2));
+          esum += key < p.n ? e : 0.f;
+        }
+      }
+    }
+    if (s % C::SPB == C::SPB - 1) {
+      const float tot = wave_active ? wave_sum(esum) : 0.f;
+      if (lane == 0) part[wave * p.nb + s / C::SPB] = tot;
+      esum = 0.f;
+    }
+    k0_cur = k0_next;
+  }
+  __syncthreads();
+  float* eg = p.energy + (((int64_t)b * p.heads + h) * p.nb + qb) * p.nb;
+  for (int kb = tid; kb < p.nb; kb += C::NT) {
+    float e = 0.f;
+    for (int w = 0; w < C::NW; ++w) e += part[w * p.nb + kb];
+    eg[kb] = e;
+  }
+}
+
+template <int D, int B>
+hipError_t launch_attn_t(const AttnParams& p, bool with_pv, hipStream_t stream) {
+  using C = Cfg<D, B>;
+  const size_t lds = (size_t)(with_pv ? 4 : 2) * C::TILE * sizeof(bfraw);
+  const dim3 grid((unsigned)((int64_t)p.n_rows * p.batch)), block(C::NT);
+  void (*kern)(AttnParams);
+  if (!with_pv) {
+    kern = attn_bf16_kernel<D, B, false, true>;
+  } else {
+    kern = p.lse ? attn_bf16_kernel<D, B, true, true> : attn_bf16_kernel<D, B, true, false>;
+  }
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  AttnParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel((const void*)kern, grid, block, args, lds, stream);
+}
+
+template <int D, int B>
+hipError_t launch_energy_t(const AttnParams& p, hipStream_t stream) {
+  using C = Cfg<D, B>;
+  const size_t lds = (size_t)2 * C::TILE * sizeof(bfraw) + (size_t)C::NW * p.nb * sizeof(float);
+  const dim3 grid((unsigned)((int64_t)p.heads * p.nb * p.batch)), block(C::NT);
+  auto kern = energy_bf16_kernel<D, B>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  AttnParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel((const void*)kern, grid, block, args, lds, stream);
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block, bool with_pv, hipStream_t stream) {
+#define CBA_CASE(D, B) \
+  if (head_dim == D && block == B) return launch_attn_t<D, B>(p, with_pv, stream);
+  CBA_CASE(64, 32) CBA_CASE(64, 64) CBA_CASE(64, 128)
+  CBA_CASE(128, 32) CBA_CASE(128, 64) CBA_CASE(128, 128)
+#undef CBA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_energy_bf16(const AttnParams& p, int head_dim, int block, hipStream_t stream) {
+#define CBA_CASE(D, B) \
+  if (head_dim == D && block == B) return launch_energy_t<D, B>(p, stream);
+  CBA_CASE(64, 32) CBA_CASE(64, 64) CBA_CASE(64, 128)
+  CBA_CASE(128, 32) CBA_CASE(128, 64) CBA_CASE(128, 128)
+#undef CBA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cba

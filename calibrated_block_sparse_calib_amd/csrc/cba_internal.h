@@ -1,0 +1,56 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer of
+// libcalibattn.so.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cba {
+
+constexpr int kMaxRepHeads = 1024;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Everything an attention-shaped kernel needs: tensor pointers and strides, the
+// problem shape, the optional skip list and the repetition-head description.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;        // may be null (energy sweep 1 without V)
+  float* lse;     // may be null
+  float* energy;  // energy sweep 2 output [batch, heads, nb, nb]
+  int64_t sb, sh, sn;  // element strides of Q/K/V/O
+  int batch, heads, n, nb;
+  int n_prefix, gf, gh, gw;
+  float c;  // softmax scale * log2(e): scores are handled in base-2 units
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t col_len;
+  const int32_t* work_order;
+  int n_rows;      // heads * nb
+  int anchor_stride;
+  int has_rep;
+  int fuse_broadcast;
+  uint32_t rep_bits[kMaxRepHeads / 32];
+};
+
+__host__ __device__ inline bool rep_head(const AttnParams& p, int h) {
+  return p.has_rep && ((p.rep_bits[h >> 5] >> (h & 31)) & 1u);
+}
+
+// Launchers (each enqueues on `stream` and returns the launch status).
+// Attention over the key blocks listed in p.row_ptr/p.col_idx, or over every key
+// block when p.row_ptr is null (dense).  with_pv = false computes only the LSE.
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block, bool with_pv, hipStream_t stream);
+hipError_t launch_energy_bf16(const AttnParams& p, int head_dim, int block, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, int head_dim, int block, bool with_pv, hipStream_t stream);
+hipError_t launch_energy_f32(const AttnParams& p, int head_dim, int block, hipStream_t stream);
+hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, double tau, double rho,
+                         int force_diag, int n_prefix_blocks, uint8_t* mask, int32_t* votes,
+                         hipStream_t stream);
+hipError_t launch_csr(const uint8_t* mask, int n_rows, int nkb, int32_t* row_ptr, int32_t* col_idx,
+                      int64_t capacity, int32_t* work_order, hipStream_t stream);
+hipError_t launch_broadcast(const AttnParams& p, int head_dim, int elem_bytes, hipStream_t stream);
+
+}  // namespace cba
