@@ -1,0 +1,288 @@
+"""Benchmark of calibrated block-sparse attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan14_720p]
+
+Workload (default): Wan-2.1-14B-like 720p self-attention -- 40 heads, head_dim 128,
+token grid 21x45x80 = 75600 tokens, bf16, block 128; per-head Bernoulli block masks
+with density uniform in 20-50% and the diagonal kept; 10 spatial-repetition heads
+with anchors every 4 image rows.  Inputs are synthetic (seeded generator) and
+resident in HBM before the timed region.
+
+A step is the inference path: build_block_csr (mask -> skip list and work order)
+then sparse_attn_fwd (kept blocks only, anchor rows of repetition heads, fused
+broadcast).  value = kept-block FLOPs / step time.  The other entry points
+(calib_block_energy, select_blocks_by_energy, rep_row_broadcast, dense_attn_fwd)
+are timed in the same run and reported under "rows"; dense_attn_fwd gives the
+speedup.  The fp64 CPU oracle is timed on a bounded sample of query blocks of the
+same workload (cpu_baseline) and its outputs are compared with the GPU's.
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "kept-block attn TFLOP/s & % bf16 MFMA peak; speedup vs dense, Wan-14B 720p"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "calibrated_block_sparse_calib_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_wan14_720p_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kept_flops(mask, cfg, rep, computed):
+    """4 d * sum over heads and computed query rows of the kept key tokens of the row's block."""
+    n, B, nb = cfg.seq_len, cfg.block, cfg.nb
+    sizes = np.minimum(B, n - np.arange(nb) * B).astype(np.int64)  # tokens per block
+    kept_tokens = mask.astype(np.int64) @ sizes  # [H, nb]
+    total = 0
+    for h in range(cfg.heads):
+        rows = computed[1] if rep[h] else computed[0]  # computed rows per query block
+        total += int((rows * kept_tokens[h]).sum())
+    return 4 * cfg.head_dim * total
+
+
+def rows_per_block(cfg, is_rep):
+    """Computed query rows per query block: all rows, or for a repetition head the
+    text rows and the image rows with y % anchor_stride == 0."""
+    r = np.ones(cfg.seq_len, bool)
+    if is_rep:
+        f_, h_, w_ = cfg.grid
+        t = np.arange(cfg.n_prefix, cfg.seq_len)
+        r[cfg.n_prefix:] = (((t - cfg.n_prefix) // w_) % h_) % cfg.anchor_stride == 0
+    pad = cfg.nb * cfg.block - cfg.seq_len
+    return np.concatenate([r, np.zeros(pad, bool)]).reshape(cfg.nb, cfg.block).sum(1).astype(np.int64)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.dirname(KERNEL_SOURCE))):
+        with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    return t.get("bytes_per_launch") if t.get("source_hash") == source_hash() else None
+
+
+def cpu_baseline(cfg, q, k, v, mask, rep, got_o, budget_s, seed=0):
+    """Time the fp64 oracle on sampled query blocks of the same workload."""
+    import oracle
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(seed)
+    nb, B = cfg.nb, cfg.block
+    picks = [(h, qb) for h in range(cfg.heads) for qb in (0, nb - 1)]  # first and ragged last blocks
+    picks += [(int(h), int(qb)) for h, qb in zip(rng.integers(0, cfg.heads, 4096), rng.integers(0, nb, 4096))]
+    comp_all = np.ones(cfg.seq_len, bool)
+    comp_rep = oracle.computed_rows(cfg.seq_len, cfg.n_prefix, cfg.grid, cfg.anchor_stride, True)
+    flops, errs, done = 0, [], 0
+    t0 = time.perf_counter()
+    for h, qb in picks:
+        if time.perf_counter() - t0 > budget_s:
+            break
+        lo, hi = qb * B, min(cfg.seq_len, (qb + 1) * B)
+        rows = np.zeros(cfg.seq_len, bool)
+        rows[lo:hi] = (comp_rep if rep[h] else comp_all)[lo:hi]
+        o, _ = oracle.sparse_attention(q[h], k[h], v[h], mask[h], B, None, rows)
+        kept = sum(min(B, cfg.seq_len - kb * B) for kb in np.nonzero(mask[h, qb])[0])
+        flops += 4 * cfg.head_dim * int(rows.sum()) * kept
+        errs.append(np.abs(got_o[h][rows] - o[rows]))
+        done += 1
+    dt = time.perf_counter() - t0
+    err = np.concatenate(errs)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{done} query blocks ({done * B} rows max) of {cfg.name}, fp64 NumPy, {dt:.1f} s",
+    }, {"rows_checked": int(err.shape[0]), "max_abs": float(err.max()), "mean_abs": float(err.mean())}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14_720p")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="time only the step (profiling runs)")
+    ap.add_argument("--no-work-order", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import calibrated_block_sparse_calib_amd as cba
+    from workloads import get_config, make_qkv, random_block_mask, rep_head_flags
+
+    cfg = get_config(args.workload)
+    if cfg.mask_mode != "bernoulli":
+        raise SystemExit("bench.py times the seeded-mask workloads; calibrated workloads are parity cases")
+    cba.load_library()
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    q, k, v = make_qkv(cfg, draw=cfg.calib_draws)
+    mask = random_block_mask(cfg)
+    rep = rep_head_flags(cfg)
+    log(f"generated {cfg.name} inputs in {time.perf_counter() - t0:.1f} s")
+    dev = lambda x: torch.from_numpy(x)[None].to(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    md = torch.from_numpy(mask).cuda()
+    od = torch.empty_like(qd)
+    B, nb, n = cfg.block, cfg.nb, cfg.seq_len
+    row_ptr = torch.empty(cfg.heads * nb + 1, dtype=torch.int32, device="cuda")
+    col_idx = torch.empty(cfg.heads * nb * nb, dtype=torch.int32, device="cuda")
+    order = torch.empty(cfg.heads * nb, dtype=torch.int32, device="cuda")
+    comp = (rows_per_block(cfg, False), rows_per_block(cfg, True))
+    flops = kept_flops(mask, cfg, rep, comp)
+    dense_flops = 4 * cfg.head_dim * n * n * cfg.heads
+    density = float(mask.mean())
+    lib = cba.load_library()
+    import ctypes
+
+    desc = cba.make_desc(qd, B, cfg.n_prefix, cfg.grid)
+    rep_arr = np.ascontiguousarray(rep)
+    stream = torch.cuda.current_stream()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    S = ctypes.c_void_p(stream.cuda_stream)
+    wo = None if args.no_work_order else P(order)
+
+    def csr():
+        st = lib.build_block_csr(P(md), cfg.heads * nb, nb, P(row_ptr), P(col_idx), col_idx.numel(), wo, S)
+        assert st == 0, st
+
+    def sparse(fuse=1):
+        st = lib.sparse_attn_fwd(ctypes.byref(desc), P(qd), P(kd), P(vd), P(row_ptr), P(col_idx), col_idx.numel(),
+                                 wo, rep_arr.ctypes.data_as(ctypes.c_void_p), cfg.anchor_stride, fuse, P(od),
+                                 None, S)
+        assert st == 0, st
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        csr()
+        sparse()
+    torch.cuda.synchronize()
+    marks = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for a, b_, c in marks:
+        a.record(stream)
+        csr()
+        b_.record(stream)
+        sparse()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    csr_ms = [a.elapsed_time(b_) for a, b_, _ in marks]
+    sparse_ms = [b_.elapsed_time(c) for _, b_, c in marks]
+    step_ms = [a.elapsed_time(c) for a, _, c in marks]
+    sp_avg = statistics.mean(sparse_ms)
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (sp_avg * 1e-3) / 1e12
+    log(f"step {wall_ms:.3f} ms wall, sparse_attn_fwd {sp_avg:.3f} ms avg ({achieved:.1f} TFLOP/s kept), "
+        f"csr {statistics.mean(csr_ms):.3f} ms")
+    got_o = od[0].float().cpu().numpy()
+
+    rows = {}
+    if not args.no_rows:
+        def timeit(fn, reps=3):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b_ = ev(), ev()
+                a.record(stream)
+                fn()
+                b_.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b_))
+            return statistics.median(ts)
+
+        do = torch.empty_like(qd)
+        dense_ms = timeit(lambda: cba.dense_attn_fwd(qd, kd, vd, block=B, o=do))
+        rows["dense_attn_fwd"] = {"ms": dense_ms, "tflops": dense_flops / dense_ms / 1e9}
+        rows["sparse_attn_fwd"] = {"ms": sp_avg, "tflops": achieved, "kept_flops": flops, "density": density}
+        rows["build_block_csr"] = {"ms": statistics.mean(csr_ms),
+                                   "algorithmic_bytes": int(mask.size + 4 * (row_ptr.numel() + 2 * int(mask.sum())
+                                                                             + order.numel()))}
+        rows["build_block_csr"]["gbs"] = rows["build_block_csr"]["algorithmic_bytes"] / rows["build_block_csr"]["ms"] / 1e6
+        bc_ms = timeit(lambda: cba.rep_row_broadcast(od, rep, cfg.anchor_stride, block=B, n_prefix=cfg.n_prefix,
+                                                     grid=cfg.grid))
+        f_, h_, w_ = cfg.grid
+        followers = int(rep.sum()) * f_ * (h_ - len(range(0, h_, cfg.anchor_stride))) * w_
+        bc_bytes = 2 * followers * cfg.head_dim * 2
+        rows["rep_row_broadcast"] = {"ms": bc_ms, "algorithmic_bytes": bc_bytes, "gbs": bc_bytes / bc_ms / 1e6}
+        unfused_ms = timeit(lambda: sparse(fuse=0))
+        rows["sparse_attn_fwd_unfused"] = {"ms": unfused_ms}
+        energy = torch.empty((1, cfg.heads, nb, nb), dtype=torch.float32, device="cuda")
+        lse = torch.empty((1, cfg.heads, n), dtype=torch.float32, device="cuda")
+        eo = torch.empty_like(qd)
+        en_ms = timeit(lambda: cba.calib_block_energy(qd, kd, vd, block=B, lse=lse, energy=energy, o=eo), reps=2)
+        rows["calib_block_energy"] = {"ms": en_ms, "draws": 1, "tflops": 1.5 * dense_flops / en_ms / 1e9}
+        sel_ms = timeit(lambda: cba.select_blocks_by_energy(energy, 0.95, 0.5))
+        rows["select_blocks_by_energy"] = {"ms": sel_ms, "draws": 1}
+        del do, eo
+
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(cfg, q, k, v, mask, rep, got_o, args.cpu_budget)
+        log(f"cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} cores; sampled parity {parity}")
+
+    traffic = traffic_from_profile()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded token-grid generator; random-init, no model weights)",
+        "config": {"workload": cfg.name, "heads": cfg.heads, "seq_len": n, "head_dim": cfg.head_dim,
+                   "grid": list(cfg.grid), "block": B, "mask_density": round(density, 4),
+                   "rep_heads": int(rep.sum()), "anchor_stride": cfg.anchor_stride,
+                   "work_order": not args.no_work_order},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "speedup_vs_dense": round(rows["dense_attn_fwd"]["ms"] / wall_ms, 3) if rows else None,
+        "roofline": {"bound": "mfma", "kernel": "sparse_attn_fwd", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
