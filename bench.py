@@ -130,7 +130,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="time only the step (profiling runs)")
-    ap.add_argument("--no-work-order", action="store_true")
+    ap.add_argument("--order", choices=["lpt", "natural"], default="natural",
+                    help="lpt: work_order from build_block_csr (longest rows first); natural: no work_order "
+                         "(rows in head-major order)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -171,10 +175,11 @@ def main():
     stream = torch.cuda.current_stream()
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     S = ctypes.c_void_p(stream.cuda_stream)
-    wo = None if args.no_work_order else P(order)
+    wo = P(order) if args.order == "lpt" else None
 
     def csr():
-        st = lib.build_block_csr(P(md), cfg.heads * nb, nb, P(row_ptr), P(col_idx), col_idx.numel(), wo, S)
+        st = lib.build_block_csr(P(md), cfg.heads * nb, nb, P(row_ptr), P(col_idx), col_idx.numel(),
+                                 P(order) if args.order == "lpt" else None, S)
         assert st == 0, st
 
     def sparse(fuse=1):
@@ -208,6 +213,14 @@ def main():
     log(f"step {wall_ms:.3f} ms wall, sparse_attn_fwd {sp_avg:.3f} ms avg ({achieved:.1f} TFLOP/s kept), "
         f"csr {statistics.mean(csr_ms):.3f} ms")
     got_o = od[0].float().cpu().numpy()
+    if args.copy_probe_mib:
+        src_t = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        for _ in range(2):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written per copy, 2 copies")
+        del src_t, dst_t
 
     rows = {}
     if not args.no_rows:
@@ -271,7 +284,7 @@ def main():
         "config": {"workload": cfg.name, "heads": cfg.heads, "seq_len": n, "head_dim": cfg.head_dim,
                    "grid": list(cfg.grid), "block": B, "mask_density": round(density, 4),
                    "rep_heads": int(rep.sum()), "anchor_stride": cfg.anchor_stride,
-                   "work_order": not args.no_work_order},
+                   "schedule": args.order},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "speedup_vs_dense": round(rows["dense_attn_fwd"]["ms"] / wall_ms, 3) if rows else None,
         "roofline": {"bound": "mfma", "kernel": "sparse_attn_fwd", "achieved": round(achieved, 2),

@@ -22,19 +22,12 @@
 // the rescale.  Numerator and denominator always share the same reference, so
 // the result is the exact softmax up to rounding.
 #include "cba_internal.h"
+#include "mfma_util.h"
 
 namespace cba {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint16_t bfraw;
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kLazyRescale = 8.0f;
+using namespace dev;
 
 template <int D, int B>
 struct Cfg {
@@ -42,90 +35,19 @@ struct Cfg {
   static constexpr int NT = NW * 64;             // threads
   static constexpr int KT = B < 64 ? B : 64;     // keys per step
   static constexpr int SPB = B / KT;             // steps per key block
-  static constexpr int RS = D + 16;              // LDS row stride (elements): 32-byte pad
-  static constexpr int TILE = KT * RS;           // elements in one K or V tile
-  static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int CPT = KT * CPR / NT;      // chunks per thread per tile
+  static constexpr int TILE = KT * D;            // elements per K or V tile
   static constexpr int KS = D / 16;              // k-steps of the QK^T product
   static constexpr int DT = D / 32;              // 32-wide d tiles of O
   static constexpr int ST = KT / 32;             // 32-key score tiles per step
-  static_assert(KT * CPR % NT == 0, "tile chunks must divide evenly");
 };
 
-// Value held by lane (l ^ 32).
-__device__ inline float other_half(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
-
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
-__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// p points into LDS: the explicit address-space casts make the compiler emit
-// ds_read instructions rather than flat loads.
-__device__ inline bf16x8 lds_read8(const bfraw* p) {
-  return *(const LDS_AS bf16x8*)(p);
-}
-
-__device__ inline i16x4 lds_read_tr(const bfraw* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p));
-}
-
-// Token rows of query block qb that this workgroup computes.  Normal heads: all
-// rows.  Repetition heads: text rows and the anchor image rows (y % stride == 0).
-// Writes the compacted in-block offsets to rowlist and returns their count.
-template <int B, int NT>
-__device__ int build_rowlist(const AttnParams& p, int q0, bool rep, int* rowlist, int* wcnt) {
-  if (!rep) return min(B, p.n - q0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  bool flag = false;
-  if (tid < B) {
-    const int tok = q0 + tid;
-    if (tok < p.n) {
-      if (tok < p.n_prefix) {
-        flag = true;
-      } else {
-        const int y = ((tok - p.n_prefix) / p.gw) % p.gh;
-        flag = (y % p.anchor_stride) == 0;
-      }
-    }
-  }
-  const uint64_t bal = __ballot(flag);
-  const int before = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) wcnt[wave] = __popcll(bal);
-  __syncthreads();
-  int off = 0, total = 0;
-  for (int w = 0; w < NT / 64; ++w) {
-    off += (w < wave) ? wcnt[w] : 0;
-    total += wcnt[w];
-  }
-  if (flag) rowlist[off + before] = tid;
-  __syncthreads();
-  return total;
-}
-
-// PV: compute O (otherwise only the log-sum-exp, for the energy sweep).
-// LSE: keep the exact fp32 row sum for the log-sum-exp output.
-// O is normalised by the sum of the same bf16-rounded weights that multiply V, so
-// rounding the weights perturbs a convex combination instead of scaling it.
+// One work item: query block qb of head h (row = h * nb + qb) for batch item b.
+// Every barrier inside is reached by all threads of the workgroup; the only early
+// exits are before the first barrier (uniform) or after the last one.
 template <int D, int B, bool PV, bool LSE>
-__global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParams p) {
+__device__ void attn_item(const AttnParams& p, int row, int b, bfraw* lds, int* rowlist, int* wcnt) {
   using C = Cfg<D, B>;
-  extern __shared__ __attribute__((aligned(16))) bfraw lds[];
-  __shared__ int rowlist[B];
-  __shared__ int wcnt[4];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-  const int item = blockIdx.x;
-  const int it = item / p.batch, b = item - it * p.batch;
-  const int row = p.work_order ? p.work_order[it] : it;
   if (row < 0 || row >= p.n_rows) return;
   const int h = row / p.nb, qb = row - h * p.nb;
   const int q0 = qb * B;
@@ -169,34 +91,6 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
     return k0 < p.n ? k0 : -1;
   };
 
-  uint4 kreg[C::CPT], vreg[PV ? C::CPT : 1];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int idx = tid + c * C::NT;
-      const int r = idx / C::CPR, col = idx - r * C::CPR;
-      const int key = k0 + r;
-      if (k0 >= 0 && key < p.n) {
-        kreg[c] = *reinterpret_cast<const uint4*>(kg + (int64_t)key * p.sn + col * 8);
-        if (PV) vreg[c] = *reinterpret_cast<const uint4*>(vg + (int64_t)key * p.sn + col * 8);
-      } else {
-        kreg[c] = make_uint4(0, 0, 0, 0);
-        if (PV) vreg[c] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    bfraw* kt = lds + buf * C::TILE;
-    bfraw* vt = lds + (2 + buf) * C::TILE;
-#pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int idx = tid + c * C::NT;
-      const int r = idx / C::CPR, col = idx - r * C::CPR;
-      *reinterpret_cast<uint4*>(kt + r * C::RS + col * 8) = kreg[c];
-      if (PV) *reinterpret_cast<uint4*>(vt + r * C::RS + col * 8) = vreg[c];
-    }
-  };
-
   f32x16 oacc[PV ? C::DT : 1];
 #pragma unroll
   for (int dt = 0; dt < (PV ? C::DT : 1); ++dt) oacc[dt] = f32x16{};
@@ -205,17 +99,24 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
   float r_part = 0.f;        // this lane's share of the rounded-weight sum (O)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+  // K tile of step s in lds[(s & 1) * TILE], V tile in lds[(2 + (s & 1)) * TILE].
+  auto load = [&](int k0, int buf) {
+    load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0, lds + buf * C::TILE);
+    if (PV) load_tile<D, C::KT, C::NW>(vg, p.sn, p.n, k0, lds + (2 + buf) * C::TILE);
+  };
   int k0_cur = nsteps > 0 ? step_key0(0) : -1;
-  if (nsteps > 0) gload(k0_cur);
+  if (nsteps > 0) load(k0_cur, 0);
 
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
-    lstore(buf);
+    // This wave's loads of tile s are complete; after the barrier everyone's are,
+    // and every wave is done reading the other buffer (step s - 1).
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int k0_next = -1;
     if (s + 1 < nsteps) {
       k0_next = step_key0(s + 1);
-      gload(k0_next);
+      load(k0_next, buf ^ 1);
     }
     if (wave_active && k0_cur >= 0) {
       const bfraw* kt = lds + buf * C::TILE;
@@ -226,7 +127,7 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
         sacc[t] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 a = lds_read8(kt + (t * 32 + (lane & 31)) * C::RS + ks * 16 + g * 8);
+          const bf16x8 a = lds_read8(kt + tile_off<D>(t * 32 + (lane & 31), ks * 16 + g * 8));
           sacc[t] = mfma(a, qf[ks], sacc[t]);
         }
       }
@@ -292,8 +193,8 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) {
               const int dcol = dt * 32 + (G & 1) * 16 + 4 * (li & 3);
-              const i16x4 lo = lds_read_tr(vt + krow * C::RS + dcol);
-              const i16x4 hi = lds_read_tr(vt + (krow + 8) * C::RS + dcol);
+              const i16x4 lo = lds_read_tr(vt + tile_off<D>(krow, dcol));
+              const i16x4 hi = lds_read_tr(vt + tile_off<D>(krow + 8, dcol));
               const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
               oacc[dt] = mfma(va, pb[t][k2], oacc[dt]);
             }
@@ -339,6 +240,18 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
   }
 }
 
+// One workgroup per item: item i = blockIdx.x is row work_order[i / batch] (or
+// row i / batch when there is no order) and batch item i % batch.
+template <int D, int B, bool PV, bool LSE>
+__global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParams p) {
+  extern __shared__ __attribute__((aligned(16))) bfraw lds[];
+  __shared__ int rowlist[B];
+  __shared__ int wcnt[4];
+  const int it = blockIdx.x / p.batch, b = blockIdx.x - it * p.batch;
+  const int row = p.work_order ? p.work_order[it] : it;
+  attn_item<D, B, PV, LSE>(p, row, b, lds, rowlist, wcnt);
+}
+
 // Block energy, sweep 2: E[qb, kb] = sum over the tile of exp(s_ij - lse_i), with
 // lse cached by the dense sweep.  One workgroup per (query block, batch item); each
 // wave sums its 32 rows' probabilities per key block in-lane, reduces across the
@@ -379,36 +292,18 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnPar
     const int k0 = (s / C::SPB) * B + (s % C::SPB) * C::KT;
     return k0 < p.n ? k0 : -1;
   };
-  uint4 kreg[C::CPT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int idx = tid + c * C::NT;
-      const int r = idx / C::CPR, col = idx - r * C::CPR;
-      const int key = k0 + r;
-      kreg[c] = (k0 >= 0 && key < p.n)
-                    ? *reinterpret_cast<const uint4*>(kg + (int64_t)key * p.sn + col * 8)
-                    : make_uint4(0, 0, 0, 0);
-    }
-  };
-
   float esum = 0.f;
   int k0_cur = step_key0(0);
-  gload(k0_cur);
+  load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0_cur, lds);
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
-    bfraw* kt = lds + buf * C::TILE;
-#pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int idx = tid + c * C::NT;
-      const int r = idx / C::CPR, col = idx - r * C::CPR;
-      *reinterpret_cast<uint4*>(kt + r * C::RS + col * 8) = kreg[c];
-    }
+    const bfraw* kt = lds + buf * C::TILE;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int k0_next = -1;
     if (s + 1 < nsteps) {
       k0_next = step_key0(s + 1);
-      gload(k0_next);
+      load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0_next, lds + (buf ^ 1) * C::TILE);
     }
     if (wave_active && k0_cur >= 0) {
 #pragma unroll
@@ -416,7 +311,7 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnPar
         f32x16 sacc = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 a = lds_read8(kt + (t * 32 + (lane & 31)) * C::RS + ks * 16 + g * 8);
+          const bf16x8 a = lds_read8(kt + tile_off<D>(t * 32 + (lane & 31), ks * 16 + g * 8));
           sacc = mfma(a, qf[ks], sacc);
         }
 #pragma unroll

@@ -1,0 +1,122 @@
+// Device helpers shared by the bf16 matrix-core kernels (gfx950).
+#pragma once
+
+#include "cba_internal.h"
+
+namespace cba {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t bfraw;
+#define LDS_AS __attribute__((address_space(3)))
+
+// The online softmax rescales its output only when a row maximum grows by more
+// than this many units of log2: the weights stay below 2^8, which bf16 and the
+// fp32 accumulators hold exactly as well as weights below 1.
+constexpr float kLazyRescale = 8.0f;
+
+// Value held by lane (l ^ 32).
+__device__ inline float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// p points into LDS: the explicit address-space casts make the compiler emit
+// ds_read instructions rather than flat loads.
+__device__ inline bf16x8 lds_read8(const bfraw* p) {
+  return *(const LDS_AS bf16x8*)(p);
+}
+
+__device__ inline i16x4 lds_read_tr(const bfraw* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p));
+}
+
+// K and V tiles live in LDS unpadded, KT rows of D bf16, with the 16-byte chunks
+// of row r XOR-swizzled by s(r) = 2*(r % 4) + (r / 4) % 2.  A K fragment read (8
+// lanes = 8 consecutive rows, same chunk) and a transpose read of V (16 lanes = 4
+// consecutive rows x 32 bytes) then each touch distinct LDS banks.
+__device__ inline int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+// Element offset of (row r, column d) in a swizzled tile with D columns.
+template <int D>
+__device__ inline int tile_off(int r, int d) {
+  return r * D + ((((d >> 3) ^ swz(r)) << 3) | (d & 7));
+}
+
+// Fills a KT x D tile straight from global memory (global_load_lds_dwordx4: each
+// lane's 16 bytes land at the instruction's LDS base + 16 * lane, no registers).
+// NW waves split the tile; wave load j of a wave covers 1 KB = 64 / (D / 8) rows.
+// Physical chunk i % (D/8) of row rr holds logical chunk (i % (D/8)) ^ swz(rr).
+// Rows past the end of the sequence reread the last row and an invalid step
+// (k0 < 0) reads the first rows: such keys are masked or skipped, so their
+// values only need to be finite.
+template <int D, int KT, int NW>
+__device__ inline void load_tile(const bfraw* src, int64_t sn, int n, int k0, bfraw* tile) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, LPW = KT / RPI / NW;
+  static_assert(KT % (RPI * NW) == 0, "tile rows must split evenly over the waves");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kk0 = k0 < 0 ? 0 : k0;
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int blk = wave * LPW + j;
+    const int rr = blk * RPI + lane / CPR;
+    const int col = (lane % CPR) ^ swz(rr);
+    const int64_t off = (int64_t)min(kk0 + rr, n - 1) * sn + col * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + off),
+                                     (LDS_AS void*)(tile + blk * 512), 16, 0, 0);
+  }
+}
+
+// Token rows of query block qb that this workgroup computes.  Normal heads: all
+// rows.  Repetition heads: text rows and the anchor image rows (y % stride == 0).
+// Writes the compacted in-block offsets to rowlist and returns their count.
+template <int B, int NT>
+__device__ int build_rowlist(const AttnParams& p, int q0, bool rep, int* rowlist, int* wcnt) {
+  if (!rep) return min(B, p.n - q0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bool flag = false;
+  if (tid < B) {
+    const int tok = q0 + tid;
+    if (tok < p.n) {
+      if (tok < p.n_prefix) {
+        flag = true;
+      } else {
+        const int y = ((tok - p.n_prefix) / p.gw) % p.gh;
+        flag = (y % p.anchor_stride) == 0;
+      }
+    }
+  }
+  const uint64_t bal = __ballot(flag);
+  const int before = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) wcnt[wave] = __popcll(bal);
+  __syncthreads();
+  int off = 0, total = 0;
+  for (int w = 0; w < NT / 64; ++w) {
+    off += (w < wave) ? wcnt[w] : 0;
+    total += wcnt[w];
+  }
+  if (flag) rowlist[off + before] = tid;
+  __syncthreads();
+  return total;
+}
+
+// PV: compute O (otherwise only the log-sum-exp, for the energy sweep).
+// LSE: keep the exact fp32 row sum for the log-sum-exp output.
+// O is normalised by the sum of the same bf16-rounded weights that multiply V, so
+// rounding the weights perturbs a convex combination instead of scaling it.
+}  // namespace dev
+}  // namespace cba

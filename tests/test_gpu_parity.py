@@ -43,10 +43,11 @@ def _oracle_sparse(cfg, q, k, v, mask, rep, stride):
 
 
 @pytest.mark.parametrize("d,block,grid,n_prefix", SMALL)
-@pytest.mark.parametrize("fuse", [True, False])
-def test_sparse_bf16_small(d, block, grid, n_prefix, fuse):
+@pytest.mark.parametrize("fuse,use_order", [(True, True), (False, True), (True, False)])
+def test_sparse_bf16_small(d, block, grid, n_prefix, fuse, use_order):
+    """use_order=False processes the rows in natural order."""
     cfg = _small_cfg(d, block, grid, n_prefix)
-    log(f"sparse bf16 d={d} B={block} grid={grid} prefix={n_prefix} fuse={fuse}")
+    log(f"sparse bf16 d={d} B={block} grid={grid} prefix={n_prefix} fuse={fuse} order={use_order}")
     q, k, v = make_qkv(cfg, draw=0)
     mask = random_block_mask(cfg)
     if cfg.nb > 2:
@@ -55,7 +56,8 @@ def test_sparse_bf16_small(d, block, grid, n_prefix, fuse):
     dm = torch.from_numpy(mask).cuda()
     row_ptr, col_idx, order = cba.build_block_csr(dm)
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
-    o, lse = cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, block=block, work_order=order, rep_heads=rep,
+    o, lse = cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, block=block,
+                                 work_order=order if use_order else None, rep_heads=rep,
                                  anchor_stride=4, fuse_broadcast=fuse, n_prefix=n_prefix, grid=grid,
                                  return_lse=True)
     if not fuse:
