@@ -44,8 +44,12 @@ struct Cfg {
 // One work item: query block qb of head h (row = h * nb + qb) for batch item b.
 // Every barrier inside is reached by all threads of the workgroup; the only early
 // exits are before the first barrier (uniform) or after the last one.
+// The four tile buffers are separate LDS objects, so the compiler can tell that
+// the reads of one buffer never alias the asynchronous loads into another and
+// does not wait for those loads before reading.
 template <int D, int B, bool PV, bool LSE>
-__device__ void attn_item(const AttnParams& p, int row, int b, bfraw* lds, int* rowlist, int* wcnt) {
+__device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, bfraw* k0s, bfraw* k1s,
+                                          bfraw* v0s, bfraw* v1s, int* rowlist, int* wcnt) {
   using C = Cfg<D, B>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   if (row < 0 || row >= p.n_rows) return;
@@ -83,9 +87,16 @@ __device__ void attn_item(const AttnParams& p, int row, int b, bfraw* lds, int* 
     const int64_t end = min((int64_t)p.row_ptr[row + 1], p.col_len);
     nblk = (int)max((int64_t)0, end - beg);
   }
+  // Uniform across the wave: the skip-list reads become scalar loads.
+  beg = __builtin_amdgcn_readfirstlane(beg);
+  nblk = __builtin_amdgcn_readfirstlane(nblk);
   const int nsteps = nblk * C::SPB;
+  // The skip list is read-only for the kernel's lifetime: reading it through the
+  // constant address space lets the (uniform) reads go to the scalar unit.
+  const __attribute__((address_space(4))) int32_t* cidx =
+      (const __attribute__((address_space(4))) int32_t*)p.col_idx;
   auto step_key0 = [&](int s) -> int {
-    const int kb = dense ? s / C::SPB : p.col_idx[beg + s / C::SPB];
+    const int kb = dense ? s / C::SPB : cidx[beg + s / C::SPB];
     if (kb < 0 || kb >= p.nb) return -1;
     const int k0 = kb * B + (s % C::SPB) * C::KT;
     return k0 < p.n ? k0 : -1;
@@ -99,56 +110,67 @@ __device__ void attn_item(const AttnParams& p, int row, int b, bfraw* lds, int* 
   float r_part = 0.f;        // this lane's share of the rounded-weight sum (O)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // K tile of step s in lds[(s & 1) * TILE], V tile in lds[(2 + (s & 1)) * TILE].
-  auto load = [&](int k0, int buf) {
-    load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0, lds + buf * C::TILE);
-    if (PV) load_tile<D, C::KT, C::NW>(vg, p.sn, p.n, k0, lds + (2 + buf) * C::TILE);
+  // Even steps use buffers (k0s, v0s), odd steps (k1s, v1s).
+  auto load = [&](int k0, bfraw* kdst, bfraw* vdst) {
+    load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0, kdst);
+    if (PV) load_tile<D, C::KT, C::NW>(vg, p.sn, p.n, k0, vdst);
   };
+  // Key offsets of the current step and the next one; the one after that is read
+  // a full step ahead of its use, so the skip-list latency stays off the path.
   int k0_cur = nsteps > 0 ? step_key0(0) : -1;
-  if (nsteps > 0) load(k0_cur, 0);
+  int k0_n1 = nsteps > 1 ? step_key0(1) : -1;
+  if (nsteps > 0) load(k0_cur, k0s, v0s);
 
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
+  auto step = [&](int s, const bfraw* kt, const bfraw* vt, bfraw* kn, bfraw* vn) {
     // This wave's loads of tile s are complete; after the barrier everyone's are,
-    // and every wave is done reading the other buffer (step s - 1).
+    // and every wave is done reading the other buffers (step s - 1).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int k0_next = -1;
-    if (s + 1 < nsteps) {
-      k0_next = step_key0(s + 1);
-      load(k0_next, buf ^ 1);
-    }
+    const int k0_next = k0_n1;
+    if (s + 1 < nsteps) load(k0_next, kn, vn);
+    k0_n1 = s + 2 < nsteps ? step_key0(s + 2) : -1;
     if (wave_active && k0_cur >= 0) {
-      const bfraw* kt = lds + buf * C::TILE;
-      const bfraw* vt = lds + (2 + buf) * C::TILE;
+      const bool ragged = k0_cur + C::KT > p.n;
+      // S^T = K Q^T.  The K fragments are read PF fragments ahead of the MFMA that
+      // consumes them, so LDS latency overlaps the matrix-core work instead of
+      // stalling every MFMA.
       f32x16 sacc[C::ST];
+      constexpr int NF = C::ST * C::KS, PF = 3;
+      auto kfrag = [&](int f) {
+        return lds_read8(kt + tile_off<D>((f / C::KS) * 32 + (lane & 31), (f % C::KS) * 16 + g * 8));
+      };
+      bf16x8 kf[PF];
 #pragma unroll
-      for (int t = 0; t < C::ST; ++t) {
-        sacc[t] = f32x16{};
+      for (int f = 0; f < PF; ++f) kf[f] = kfrag(f);
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 a = lds_read8(kt + tile_off<D>(t * 32 + (lane & 31), ks * 16 + g * 8));
-          sacc[t] = mfma(a, qf[ks], sacc[t]);
-        }
+      for (int t = 0; t < C::ST; ++t) sacc[t] = f32x16{};
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const bf16x8 a = kf[f % PF];
+        if (f + PF < NF) kf[f % PF] = kfrag(f + PF);
+        sacc[f / C::KS] = mfma(a, qf[f % C::KS], sacc[f / C::KS]);
       }
-      // Keys past the end of the sequence (ragged last block) take no part.
-      if (k0_cur + C::KT > p.n) {
+      // Keys past the end of the sequence (ragged last block) take no part.  The
+      // empty asm keeps this rare block a real branch: the compiler would
+      // otherwise evaluate its compares and selects on every step.
+      if (ragged) {
+        asm volatile("" ::: "memory");
+        const int lim = p.n - k0_cur - g * 4;  // element (t, i) holds key k0 + t*32 + (i/4)*8 + g*4 + i%4
 #pragma unroll
         for (int t = 0; t < C::ST; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0_cur + t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-            if (key >= p.n) sacc[t][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (t * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[t][i] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < C::ST; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[t][i]);
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[t][i], sacc[t][i + 1]));
       mx = fmaxf(mx, other_half(mx));
       const float mt = mx * p.c;
       if (__ballot(mt > m_used + kLazyRescale)) {
+        asm volatile("" ::: "memory");  // rare: keep it a branch (see above)
         const float m_new = fmaxf(m_used, mt);
         const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
         l_part *= alpha;
@@ -202,7 +224,13 @@ __device__ void attn_item(const AttnParams& p, int row, int b, bfraw* lds, int* 
       }
     }
     k0_cur = k0_next;
+  };
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    step(s, k0s, v0s, k1s, v1s);
+    step(s + 1, k1s, v1s, k0s, v0s);
   }
+  if (s < nsteps) step(s, k0s, v0s, k1s, v1s);
 
   if (!wave_active) return;
   const float l_tot = l_part + other_half(l_part);
@@ -244,12 +272,14 @@ __device__ void attn_item(const AttnParams& p, int row, int b, bfraw* lds, int* 
 // row i / batch when there is no order) and batch item i % batch.
 template <int D, int B, bool PV, bool LSE>
 __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParams p) {
-  extern __shared__ __attribute__((aligned(16))) bfraw lds[];
+  using C = Cfg<D, B>;
+  __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bfraw v0s[PV ? C::TILE : 8], v1s[PV ? C::TILE : 8];
   __shared__ int rowlist[B];
   __shared__ int wcnt[4];
   const int it = blockIdx.x / p.batch, b = blockIdx.x - it * p.batch;
   const int row = p.work_order ? p.work_order[it] : it;
-  attn_item<D, B, PV, LSE>(p, row, b, lds, rowlist, wcnt);
+  attn_item<D, B, PV, LSE>(p, row, b, k0s, k1s, v0s, v1s, rowlist, wcnt);
 }
 
 // Block energy, sweep 2: E[qb, kb] = sum over the tile of exp(s_ij - lse_i), with
@@ -260,8 +290,8 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
 template <int D, int B>
 __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnParams p) {
   using C = Cfg<D, B>;
-  extern __shared__ __attribute__((aligned(16))) bfraw lds[];
-  float* part = reinterpret_cast<float*>(lds + 2 * C::TILE);  // [NW][nb]
+  __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
+  extern __shared__ float part[];  // [NW][nb]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int item = blockIdx.x;
@@ -294,16 +324,14 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnPar
   };
   float esum = 0.f;
   int k0_cur = step_key0(0);
-  load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0_cur, lds);
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bfraw* kt = lds + buf * C::TILE;
+  load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0_cur, k0s);
+  auto step = [&](int s, const bfraw* kt, bfraw* kn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int k0_next = -1;
     if (s + 1 < nsteps) {
       k0_next = step_key0(s + 1);
-      load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0_next, lds + (buf ^ 1) * C::TILE);
+      load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0_next, kn);
     }
     if (wave_active && k0_cur >= 0) {
 #pragma unroll
@@ -328,7 +356,13 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnPar
       esum = 0.f;
     }
     k0_cur = k0_next;
+  };
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    step(s, k0s, k1s);
+    step(s + 1, k1s, k0s);
   }
+  if (s < nsteps) step(s, k0s, k1s);
   __syncthreads();
   float* eg = p.energy + (((int64_t)b * p.heads + h) * p.nb + qb) * p.nb;
   for (int kb = tid; kb < p.nb; kb += C::NT) {
@@ -341,7 +375,7 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnPar
 template <int D, int B>
 hipError_t launch_attn_t(const AttnParams& p, bool with_pv, hipStream_t stream) {
   using C = Cfg<D, B>;
-  const size_t lds = (size_t)(with_pv ? 4 : 2) * C::TILE * sizeof(bfraw);
+  const size_t lds = 0;  // static tile buffers
   const dim3 grid((unsigned)((int64_t)p.n_rows * p.batch)), block(C::NT);
   void (*kern)(AttnParams);
   if (!with_pv) {
@@ -359,7 +393,7 @@ hipError_t launch_attn_t(const AttnParams& p, bool with_pv, hipStream_t stream) 
 template <int D, int B>
 hipError_t launch_energy_t(const AttnParams& p, hipStream_t stream) {
   using C = Cfg<D, B>;
-  const size_t lds = (size_t)2 * C::TILE * sizeof(bfraw) + (size_t)C::NW * p.nb * sizeof(float);
+  const size_t lds = (size_t)C::NW * p.nb * sizeof(float);
   const dim3 grid((unsigned)((int64_t)p.heads * p.nb * p.batch)), block(C::NT);
   auto kern = energy_bf16_kernel<D, B>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
