@@ -82,8 +82,8 @@ CONFIGS = {
         block=128,
         dtype="bf16",
         seed=1,
-        lt=6.0,
-        ls=14.0,
+        lt=15.86,
+        ls=37.0,
         mask_mode="calibrate",
         calib_draws=4,
         tau=0.95,
@@ -97,8 +97,8 @@ CONFIGS = {
         block=128,
         dtype="bf16",
         seed=2,
-        lt=6.0,
-        ls=14.0,
+        lt=15.86,
+        ls=37.0,
         mask_mode="bernoulli",
         density_range=(0.2, 0.5),
         n_rep_heads=10,
@@ -114,8 +114,8 @@ CONFIGS = {
         dtype="bf16",
         seed=3,
         n_prefix=256,
-        lt=6.0,
-        ls=14.0,
+        lt=15.86,
+        ls=37.0,
         mask_mode="calibrate",
         calib_draws=4,
         tau=0.95,
@@ -131,9 +131,9 @@ CONFIGS = {
         block=128,
         dtype="bf16",
         seed=4,
-        lt=6.0,
-        ls=14.0,
-        ls_log_range=(0.5, 2.0),
+        lt=24.86,
+        ls=58.0,
+        ls_log_range=(0.5, 2.1),
         mask_mode="calibrate",
         calib_draws=4,
         tau=0.95,
