@@ -11,6 +11,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: takes more than a few seconds")
+    # Mutation runs (tests/test_oracle_mutations.py) plant one mistake in the oracle.
+    mutant = os.environ.get("CALIBATTN_ORACLE_MUTANT")
+    if mutant:
+        from tests import oracle_mutants
+
+        oracle_mutants.apply(mutant)
 
 
 def pytest_collection_modifyitems(config, items):
