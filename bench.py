@@ -19,6 +19,7 @@ same workload (cpu_baseline) and its outputs are compared with the GPU's.
 Prints one JSON line.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -121,6 +122,46 @@ def cpu_baseline(cfg, q, k, v, mask, rep, got_o, budget_s, seed=0):
     }, {"rows_checked": int(err.shape[0]), "max_abs": float(err.max()), "mean_abs": float(err.mean())}
 
 
+def density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S,
+                  densities=(0.10, 0.20, 0.35, 0.50, 1.0)):
+    """sparse_attn_fwd on the same shape with one seeded Bernoulli density for every
+    head (diagonal kept, no repetition heads); least-squares fit of time against
+    kept FLOPs shows whether time scales with the kept work."""
+    import dataclasses
+
+    import torch
+    from workloads import random_block_mask
+
+    points = []
+    full_rows = rows_per_block(cfg, False)
+    no_rep = np.zeros(cfg.heads, bool)
+    for dens in densities:
+        c = dataclasses.replace(cfg, density_range=(dens, dens))
+        m = random_block_mask(c) if dens < 1.0 else np.ones((cfg.heads, cfg.nb, cfg.nb), np.uint8)
+        md = torch.from_numpy(m).cuda()
+        st = lib.build_block_csr(P(md), cfg.heads * cfg.nb, cfg.nb, P(row_ptr), P(col_idx), col_idx.numel(), None, S)
+        assert st == 0, st
+
+        def run():
+            st = lib.sparse_attn_fwd(ctypes.byref(desc), P(qd), P(kd), P(vd), P(row_ptr), P(col_idx),
+                                     col_idx.numel(), None, None, cfg.anchor_stride, 0, P(od), None, S)
+            assert st == 0, st
+
+        ms = timeit(run)
+        fl = kept_flops(m, cfg, no_rep, (full_rows, full_rows))
+        points.append({"density": round(float(m.mean()), 4), "ms": ms, "kept_flops": fl,
+                       "tflops": fl / ms / 1e9})
+        del md
+    x = np.array([p["kept_flops"] for p in points], float)
+    y = np.array([p["ms"] for p in points], float)
+    slope, icpt = np.polyfit(x, y, 1)
+    r2 = 1.0 - float(((y - (slope * x + icpt)) ** 2).sum() / ((y - y.mean()) ** 2).sum())
+    log("density sweep: " + ", ".join(f"{p['density']:.2f}: {p['ms']:.2f} ms" for p in points) +
+        f"; fit r2 {r2:.5f}")
+    return {"points": points, "fit_ms_per_tflop": slope * 1e12, "fit_intercept_ms": icpt, "fit_r2": r2,
+            "marginal_tflops": 1e-9 / slope}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +174,7 @@ def main():
     ap.add_argument("--order", choices=["lpt", "natural"], default="natural",
                     help="lpt: work_order from build_block_csr (longest rows first); natural: no work_order "
                          "(rows in head-major order)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the density sweep")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -168,8 +210,6 @@ def main():
     dense_flops = 4 * cfg.head_dim * n * n * cfg.heads
     density = float(mask.mean())
     lib = cba.load_library()
-    import ctypes
-
     desc = cba.make_desc(qd, B, cfg.n_prefix, cfg.grid)
     rep_arr = np.ascontiguousarray(rep)
     stream = torch.cuda.current_stream()
@@ -260,7 +300,9 @@ def main():
         rows["calib_block_energy"] = {"ms": en_ms, "draws": 1, "tflops": 1.5 * dense_flops / en_ms / 1e9}
         sel_ms = timeit(lambda: cba.select_blocks_by_energy(energy, 0.95, 0.5))
         rows["select_blocks_by_energy"] = {"ms": sel_ms, "draws": 1}
-        del do, eo
+        del do, eo, energy
+        if not args.no_sweep:
+            rows["density_sweep"] = density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S)
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
