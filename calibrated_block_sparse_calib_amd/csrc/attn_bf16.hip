@@ -47,7 +47,7 @@ struct Cfg {
 // The four tile buffers are separate LDS objects, so the compiler can tell that
 // the reads of one buffer never alias the asynchronous loads into another and
 // does not wait for those loads before reading.
-template <int D, int B, bool PV, bool LSE>
+template <int D, int B, bool PV, bool LSE, bool BUF>
 __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, bfraw* k0s, bfraw* k1s,
                                           bfraw* v0s, bfraw* v1s, int* rowlist, int* wcnt) {
   using C = Cfg<D, B>;
@@ -111,9 +111,23 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Even steps use buffers (k0s, v0s), odd steps (k1s, v1s).
+  // BUF: tiles come by buffer loads with per-lane offsets fixed for the whole
+  // item (byte offsets fit 32 bits); otherwise by global loads with the row
+  // clamped to the sequence.
+  constexpr int LPW = C::KT / (64 / (D / 8)) / C::NW;
+  int voff[LPW];
+  if (BUF) tile_lane_offsets<D, C::KT, C::NW>((int)(p.sn * 2), voff);
+  const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto load = [&](int k0, bfraw* kdst, bfraw* vdst) {
-    load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0, kdst);
-    if (PV) load_tile<D, C::KT, C::NW>(vg, p.sn, p.n, k0, vdst);
+    if (BUF) {
+      const int so = k0 * (int)(p.sn * 2);
+      load_tile_buf(kg, nrec, voff, LPW, so, kdst + wv * LPW * 512);
+      if (PV) load_tile_buf(vg, nrec, voff, LPW, so, vdst + wv * LPW * 512);
+    } else {
+      load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0, kdst);
+      if (PV) load_tile<D, C::KT, C::NW>(vg, p.sn, p.n, k0, vdst);
+    }
   };
   // Key offsets of the current step and the next one; the one after that is read
   // a full step ahead of its use, so the skip-list latency stays off the path.
@@ -270,7 +284,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
 
 // One workgroup per item: item i = blockIdx.x is row work_order[i / batch] (or
 // row i / batch when there is no order) and batch item i % batch.
-template <int D, int B, bool PV, bool LSE>
+template <int D, int B, bool PV, bool LSE, bool BUF>
 __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParams p) {
   using C = Cfg<D, B>;
   __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
@@ -279,7 +293,7 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
   __shared__ int wcnt[4];
   const int it = blockIdx.x / p.batch, b = blockIdx.x - it * p.batch;
   const int row = p.work_order ? p.work_order[it] : it;
-  attn_item<D, B, PV, LSE>(p, row, b, k0s, k1s, v0s, v1s, rowlist, wcnt);
+  attn_item<D, B, PV, LSE, BUF>(p, row, b, k0s, k1s, v0s, v1s, rowlist, wcnt);
 }
 
 // Block energy, sweep 2: E[qb, kb] = sum over the tile of exp(s_ij - lse_i), with
@@ -287,7 +301,7 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
 // wave sums its 32 rows' probabilities per key block in-lane, reduces across the
 // wave, and the per-wave partials are added in wave order at the end, so the
 // result is deterministic.
-template <int D, int B>
+template <int D, int B, bool BUF>
 __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnParams p) {
   using C = Cfg<D, B>;
   __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
@@ -322,33 +336,52 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnPar
     const int k0 = (s / C::SPB) * B + (s % C::SPB) * C::KT;
     return k0 < p.n ? k0 : -1;
   };
+  constexpr int LPW = C::KT / (64 / (D / 8)) / C::NW;
+  int voff[LPW];
+  if (BUF) tile_lane_offsets<D, C::KT, C::NW>((int)(p.sn * 2), voff);
+  const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto load = [&](int k0, bfraw* kdst) {
+    if (BUF) load_tile_buf(kg, nrec, voff, LPW, k0 * (int)(p.sn * 2), kdst + wv * LPW * 512);
+    else load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0, kdst);
+  };
   float esum = 0.f;
   int k0_cur = step_key0(0);
-  load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0_cur, k0s);
+  load(k0_cur, k0s);
   auto step = [&](int s, const bfraw* kt, bfraw* kn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int k0_next = -1;
     if (s + 1 < nsteps) {
       k0_next = step_key0(s + 1);
-      load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0_next, kn);
+      load(k0_next, kn);
     }
     if (wave_active && k0_cur >= 0) {
+      f32x16 sacc[C::ST];
 #pragma unroll
       for (int t = 0; t < C::ST; ++t) {
-        f32x16 sacc = f32x16{};
+        sacc[t] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           const bf16x8 a = lds_read8(kt + tile_off<D>(t * 32 + (lane & 31), ks * 16 + g * 8));
-          sacc = mfma(a, qf[ks], sacc);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0_cur + t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], p.c, -lse2));
-          esum += key < p.n ? e : 0.f;
+          sacc[t] = mfma(a, qf[ks], sacc[t]);
         }
       }
+      if (k0_cur + C::KT > p.n) {
+        // Ragged last step: keys at or past the end add nothing.  Element (t, i)
+        // holds key k0 + t*32 + (i/4)*8 + g*4 + i%4.
+        asm volatile("" ::: "memory");  // rare: keep it a real branch
+        const int lim = p.n - k0_cur - g * 4;
+#pragma unroll
+        for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (t * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[t][i] = -INFINITY;
+      }
+#pragma unroll
+      for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) esum += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], p.c, -lse2));
     }
     if (s % C::SPB == C::SPB - 1) {
       const float tot = wave_active ? wave_sum(esum) : 0.f;
@@ -377,11 +410,16 @@ hipError_t launch_attn_t(const AttnParams& p, bool with_pv, hipStream_t stream) 
   using C = Cfg<D, B>;
   const size_t lds = 0;  // static tile buffers
   const dim3 grid((unsigned)((int64_t)p.n_rows * p.batch)), block(C::NT);
+  // Buffer loads take 32-bit byte offsets: every key row of a head must be
+  // addressable with them.
+  const bool buf = (int64_t)(p.n + C::KT) * p.sn * 2 < ((int64_t)1 << 31);
   void (*kern)(AttnParams);
   if (!with_pv) {
-    kern = attn_bf16_kernel<D, B, false, true>;
+    kern = buf ? attn_bf16_kernel<D, B, false, true, true> : attn_bf16_kernel<D, B, false, true, false>;
+  } else if (p.lse) {
+    kern = buf ? attn_bf16_kernel<D, B, true, true, true> : attn_bf16_kernel<D, B, true, true, false>;
   } else {
-    kern = p.lse ? attn_bf16_kernel<D, B, true, true> : attn_bf16_kernel<D, B, true, false>;
+    kern = buf ? attn_bf16_kernel<D, B, true, false, true> : attn_bf16_kernel<D, B, true, false, false>;
   }
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -395,7 +433,8 @@ hipError_t launch_energy_t(const AttnParams& p, hipStream_t stream) {
   using C = Cfg<D, B>;
   const size_t lds = (size_t)C::NW * p.nb * sizeof(float);
   const dim3 grid((unsigned)((int64_t)p.heads * p.nb * p.batch)), block(C::NT);
-  auto kern = energy_bf16_kernel<D, B>;
+  const bool buf = (int64_t)(p.n + C::KT) * p.sn * 2 < ((int64_t)1 << 31);
+  auto kern = buf ? energy_bf16_kernel<D, B, true> : energy_bf16_kernel<D, B, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   AttnParams arg = p;

@@ -46,15 +46,22 @@ __device__ inline i16x4 lds_read_tr(const bfraw* p) {
 }
 
 // K and V tiles live in LDS unpadded, KT rows of D bf16, with the 16-byte chunks
-// of row r XOR-swizzled by s(r) = 2*(r % 4) + (r / 4) % 2.  A K fragment read (8
-// lanes = 8 consecutive rows, same chunk) and a transpose read of V (16 lanes = 4
-// consecutive rows x 32 bytes) then each touch distinct LDS banks.
-__device__ inline int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// of row r XOR-swizzled by s(r).  The LDS serves 256 bytes (64 banks) at a time:
+// a K fragment read puts 16 consecutive rows, same logical chunk, in one such
+// group, and a transpose read of V puts 4 consecutive rows x 4 chunks in one.
+// For 256-byte rows (D = 128), s(r) = 4*(r % 4) + (r / 4) % 4 gives 16 distinct
+// chunks over any 16 consecutive rows and 4 distinct chunk quads over any 4
+// aligned rows, so both reads are conflict-free; 128-byte rows (D = 64) use
+// s(r) = 2*(r % 4) + (r / 4) % 2 over their 8 chunks.
+template <int D>
+__device__ inline int swz(int r) {
+  return D >= 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 2 * (r & 3) + ((r >> 2) & 1);
+}
 
 // Element offset of (row r, column d) in a swizzled tile with D columns.
 template <int D>
 __device__ inline int tile_off(int r, int d) {
-  return r * D + ((((d >> 3) ^ swz(r)) << 3) | (d & 7));
+  return r * D + ((((d >> 3) ^ swz<D>(r)) << 3) | (d & 7));
 }
 
 // Fills a KT x D tile straight from global memory (global_load_lds_dwordx4: each
@@ -74,11 +81,38 @@ __device__ inline void load_tile(const bfraw* src, int64_t sn, int n, int k0, bf
   for (int j = 0; j < LPW; ++j) {
     const int blk = wave * LPW + j;
     const int rr = blk * RPI + lane / CPR;
-    const int col = (lane % CPR) ^ swz(rr);
+    const int col = (lane % CPR) ^ swz<D>(rr);
     const int64_t off = (int64_t)min(kk0 + rr, n - 1) * sn + col * 8;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + off),
                                      (LDS_AS void*)(tile + blk * 512), 16, 0, 0);
   }
+}
+
+// Buffer-load variant of load_tile, for tiles addressed with 32-bit byte offsets:
+// the lane offsets inside a tile are fixed (tile_lane_offsets, once per kernel)
+// and the tile's first key enters as one scalar offset, so a tile load costs no
+// vector instructions.  The buffer covers the nrec bytes at base; rows past it
+// read as zeros.  The resource is built here, in device-only code, because the
+// host compilation also sees kernels and their lambdas and has no
+// buffer-resource type.
+template <int D, int KT, int NW>
+__device__ inline void tile_lane_offsets(int row_bytes, int* voff) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, LPW = KT / RPI / NW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int rr = (wave * LPW + j) * RPI + lane / CPR;
+    voff[j] = rr * row_bytes + ((lane % CPR) ^ swz<D>(rr)) * 16;
+  }
+}
+
+__device__ __forceinline__ void load_tile_buf(const void* base, int nrec, const int* voff, int lpw, int so,
+                                              bfraw* dst) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec,
+                                                                      0x00020000);
+#pragma unroll
+  for (int j = 0; j < lpw; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + j * 512), 16, voff[j], so, 0, 0);
 }
 
 // Token rows of query block qb that this workgroup computes.  Normal heads: all
