@@ -57,6 +57,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
   const int q0 = qb * B;
   const bool rep = rep_head(p, h);
   const int M = build_rowlist<B, C::NT>(p, q0, rep, rowlist, wcnt);
+  // A block of a repetition head with no text or anchor row computes nothing:
+  // its rows are followers, written from their anchors' blocks.
+  if (M == 0) return;
 
   const int64_t head_off = (int64_t)b * p.sb + (int64_t)h * p.sh;
   const bfraw* qg = static_cast<const bfraw*>(p.q) + head_off;
