@@ -162,6 +162,76 @@ def density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S
             "marginal_tflops": 1e-9 / slope}
 
 
+def calibrated_workload(name, reps=2):
+    """One calibrated workload end to end: calib_block_energy over every draw
+    (LSE-only dense sweep + energy sweep), select_blocks_by_energy, build_block_csr
+    and sparse_attn_fwd on a held-out draw, plus dense_attn_fwd for the speedup.
+    Per timestep bucket when the workload has several."""
+    import torch
+
+    import calibrated_block_sparse_calib_amd as cba
+    from workloads import get_config, make_qkv
+
+    cfg = get_config(name)
+    B, n, H, d = cfg.block, cfg.seq_len, cfg.heads, cfg.head_dim
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b_ = ev(), ev()
+            a.record()
+            fn()
+            b_.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b_))
+        return statistics.median(ts)
+
+    out = []
+    for bucket in range(cfg.buckets):
+        t0 = time.perf_counter()
+        draws = [make_qkv(cfg, draw=i, bucket=bucket, with_v=False) for i in range(cfg.calib_draws)]
+        qc = dev(np.stack([x[0] for x in draws]))
+        kc = dev(np.stack([x[1] for x in draws]))
+        del draws
+        q, k, v = make_qkv(cfg, draw=cfg.calib_draws, bucket=bucket)
+        qd, kd, vd = dev(q[None]), dev(k[None]), dev(v[None])
+        del q, k, v
+        log(f"{name} bucket {bucket}: inputs generated in {time.perf_counter() - t0:.1f} s")
+        res = {}
+        energy, lse, _ = cba.calib_block_energy(qc, kc, None, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid)
+        e_ms = timed(lambda: cba.calib_block_energy(qc, kc, None, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid,
+                                                   lse=lse, energy=energy))
+        cal_flops = 4 * n * n * d * H * cfg.calib_draws  # QK^T in both sweeps
+        mask = cba.select_blocks_by_energy(energy, cfg.tau, cfg.rho, True, cfg.n_prefix_blocks)
+        s_ms = timed(lambda: cba.select_blocks_by_energy(energy, cfg.tau, cfg.rho, True, cfg.n_prefix_blocks,
+                                                        mask=mask))
+        row_ptr, col_idx, _ = cba.build_block_csr(mask, with_order=False)
+        c_ms = timed(lambda: cba.build_block_csr(mask, with_order=False))
+        o = torch.empty_like(qd)
+        sp_ms = timed(lambda: cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, block=B, n_prefix=cfg.n_prefix,
+                                                  grid=cfg.grid, o=o))
+        de_ms = timed(lambda: cba.dense_attn_fwd(qd, kd, vd, block=B, o=o))
+        m = mask.cpu().numpy()
+        kept = kept_flops(m, cfg, np.zeros(H, bool), (rows_per_block(cfg, False),) * 2)
+        dens = m.mean(axis=(1, 2))
+        res.update({"bucket": bucket, "draws": cfg.calib_draws, "calib_ms": e_ms,
+                    "calib_tflops": cal_flops / e_ms / 1e9, "select_ms": s_ms, "csr_ms": c_ms,
+                    "mask_density": float(m.mean()), "head_density_min": float(dens.min()),
+                    "head_density_max": float(dens.max()), "sparse_ms": sp_ms, "sparse_tflops": kept / sp_ms / 1e9,
+                    "dense_ms": de_ms, "speedup_vs_dense": de_ms / sp_ms})
+        log(f"{name} bucket {bucket}: calibration {e_ms:.1f} ms ({res['calib_tflops']:.0f} TFLOP/s), select "
+            f"{s_ms:.2f} ms, density {res['mask_density']:.3f}, sparse {sp_ms:.2f} ms "
+            f"({res['sparse_tflops']:.0f} TFLOP/s kept), dense {de_ms:.2f} ms")
+        out.append(res)
+        del qc, kc, qd, kd, vd, energy, lse, mask, row_ptr, col_idx, o
+        torch.cuda.empty_cache()
+    return out if len(out) > 1 else out[0]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +245,9 @@ def main():
                     help="lpt: work_order from build_block_csr (longest rows first); natural: no work_order "
                          "(rows in head-major order)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the density sweep")
+    ap.add_argument("--calibrated", default="",
+                    help="comma-separated calibrated workloads (wan13_480p, mochi, hunyuan, or 'all') to also time "
+                         "end to end: calibration over all draws, selection, skip list, sparse attention")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -303,6 +376,12 @@ def main():
         del do, eo, energy
         if not args.no_sweep:
             rows["density_sweep"] = density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S)
+
+    if args.calibrated:
+        names = ["wan13_480p", "mochi", "hunyuan"] if args.calibrated == "all" else args.calibrated.split(",")
+        del qd, kd, vd, od, md, row_ptr, col_idx, order
+        torch.cuda.empty_cache()
+        rows["calibrated"] = {name: calibrated_workload(name) for name in names}
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
