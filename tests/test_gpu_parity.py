@@ -268,3 +268,43 @@ def test_deterministic_repeat():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(e1, e2)
+
+
+def test_wide_row_stride_takes_global_load_path():
+    """Row strides so wide that a head's K/V rows need byte offsets beyond 31 bits
+    send every kernel down its global-load path (clamped rows instead of a
+    bounded buffer).  Same results, bit for bit, as the compact layout; the
+    compact layout itself is checked against the oracle above."""
+    cfg = _small_cfg(128, 128, (2, 17, 20), 0, heads=2)
+    n, d = cfg.seq_len, cfg.head_dim
+    sn = ((1 << 31) // (2 * (n + 64)) // 8 + 1) * 8  # (n + 64) * sn * 2 bytes >= 2^31
+    log(f"wide stride: n={n} stride_n={sn} ({2 * n * sn * cfg.heads / 2**30:.1f} GiB per tensor)")
+    q, k, v = make_qkv(cfg, draw=0)
+    mask = random_block_mask(cfg)
+    rep = rep_head_flags(cfg)
+    row_ptr, col_idx, _ = cba.build_block_csr(torch.from_numpy(mask).cuda())
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+
+    def wide(t):
+        w = torch.zeros((1, cfg.heads, n, sn), dtype=t.dtype, device=t.device)[..., :d]
+        w.copy_(t)
+        return w
+
+    qw, kw, vw = wide(qd), wide(kd), wide(vd)
+    assert qw.stride(2) == sn
+    ow = wide(torch.zeros_like(qd))
+    kwargs = dict(block=128, rep_heads=rep, anchor_stride=4, grid=cfg.grid)
+    o_c, l_c = cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, return_lse=True, **kwargs)
+    o_w, l_w = cba.sparse_attn_fwd(qw, kw, vw, row_ptr, col_idx, o=ow, return_lse=True, **kwargs)
+    e_c, le_c, _ = cba.calib_block_energy(qd, kd, None, block=128)
+    e_w, le_w, _ = cba.calib_block_energy(qw, kw, None, block=128)
+    d_c = cba.dense_attn_fwd(qd, kd, vd, block=128)
+    d_w = cba.dense_attn_fwd(qw, kw, vw, block=128, o=wide(torch.zeros_like(qd)))
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_w.contiguous()) and torch.equal(l_c, l_w)
+    assert torch.equal(e_c, e_w) and torch.equal(le_c, le_w)
+    assert torch.equal(d_c, d_w.contiguous())
+    ref_o, _ = _oracle_sparse(cfg, q, k, v, mask, rep, 4)
+    assert_close_out(to_host(o_w)[0], ref_o, "bf16", "wide-stride sparse O")
+    del qw, kw, vw, ow
+    torch.cuda.empty_cache()
