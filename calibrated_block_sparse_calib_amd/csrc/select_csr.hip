@@ -127,17 +127,35 @@ __global__ __launch_bounds__(64 * kWaves) void csr_count_kernel(const uint8_t* m
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 16;  // counts per thread per pass: 16 K rows per pass
+constexpr int kScanChunk = kScanThreads * kScanPer;
 
+// Padded LDS index: a thread's run of kScanPer consecutive counts then spans
+// distinct banks.
+__device__ inline int scan_slot(int i) { return i + (i >> 4); }
+
+// In-place inclusive scan of row_ptr[1 .. n_rows] (the per-row counts) by one
+// workgroup.  Each pass stages 16 K counts in LDS with coalesced loads; every
+// thread sums its own run of kScanPer counts, the workgroup scans the run totals
+// (wave scans, then the wave totals), each thread writes its run's prefixes back
+// to LDS, and the pass ends with coalesced stores.
 __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(int n_rows, int32_t* row_ptr) {
+  __shared__ int buf[kScanChunk + kScanChunk / 16];
   __shared__ int wsum[kScanThreads / 64];
-  __shared__ int carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < n_rows; base += kScanThreads) {
-    const int idx = base + tid;
-    const int v = idx < n_rows ? row_ptr[idx + 1] : 0;
-    int x = v;
+  int carry = 0;
+  for (int base = 0; base < n_rows; base += kScanChunk) {
+    const int len = min(kScanChunk, n_rows - base);
+    for (int i = tid; i < kScanChunk; i += kScanThreads) buf[scan_slot(i)] = i < len ? row_ptr[base + i + 1] : 0;
+    __syncthreads();
+    int v[kScanPer];
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      v[i] = buf[scan_slot(tid * kScanPer + i)];
+      run += v[i];
+    }
+    int x = run;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off, 64);
@@ -145,11 +163,20 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(int n_rows, int3
     }
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    int before = carry_s;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    if (idx < n_rows) row_ptr[idx + 1] = before + x;
+    int before = carry, total = carry;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      before += (w < wave) ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    int acc = before + x - run;  // exclusive prefix of this thread's run
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      acc += v[i];
+      buf[scan_slot(tid * kScanPer + i)] = acc;
+    }
     __syncthreads();
-    if (tid == kScanThreads - 1) carry_s = before + x;
+    for (int i = tid; i < len; i += kScanThreads) row_ptr[base + i + 1] = buf[scan_slot(i)];
+    carry = total;
     __syncthreads();
   }
 }
