@@ -183,8 +183,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
 #pragma unroll
       for (int t = 0; t < C::ST; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[t][i], sacc[t][i + 1]));
-      mx = fmaxf(mx, other_half(mx));
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sacc[t][i]), sacc[t][i + 1]);  // v_max3 chain
+      mx = halves_max(mx);
       const float mt = mx * p.c;
       if (__ballot(mt > m_used + kLazyRescale)) {
         asm volatile("" ::: "memory");  // rare: keep it a branch (see above)

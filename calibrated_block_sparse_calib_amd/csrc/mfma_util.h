@@ -19,6 +19,12 @@ typedef uint16_t bfraw;
 // fp32 accumulators hold exactly as well as weights below 1.
 constexpr float kLazyRescale = 8.0f;
 
+// Maximum of the values held by lanes l and l ^ 32 (the same in both lanes).
+__device__ inline float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Value held by lane (l ^ 32).
 __device__ inline float other_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
