@@ -15,6 +15,9 @@ from .calibattn_oracle import (
     row_broadcast,
     sparse_attention_with_repetition,
     token_mask_from_blocks,
+    repetition_cosines,
+    repetition_score,
+    mark_repetition_heads,
 )
 
 __all__ = [
@@ -29,4 +32,7 @@ __all__ = [
     "row_broadcast",
     "sparse_attention_with_repetition",
     "token_mask_from_blocks",
+    "repetition_cosines",
+    "repetition_score",
+    "mark_repetition_heads",
 ]

@@ -34,7 +34,13 @@ Readings of points the pages leave open (each is repeated where it is used):
      are forced kept after aggregation;
   R8 a "spatial row" is one image row (f, y) of W tokens; anchors are the rows with
      y mod s == 0 and each stands for rows y .. y+s-1 of its frame;
-  R9 an anchor row keeps its own query block's mask; text tokens are never followers.
+  R9 an anchor row keeps its own query block's mask; text tokens are never followers;
+  R10 the "attention vector" of a token is its row of dense attention probabilities
+     (softmax over all keys), and a follower token is compared with the token that
+     the broadcast copies into it: its anchor, same frame and column;
+  R11 a head's repetition score is the mean of those cosines over all follower
+     tokens; over calibration inputs the scores are averaged (fp64, input order)
+     and the head is marked when the average is strictly above gamma.
 
 Parity pins: every function is pinned by tests against library routines, closed
 forms, invariants or brute force (tests/test_oracle.py).
@@ -277,3 +283,76 @@ def sparse_attention_with_repetition(q, k, v, mask_h, block, n_prefix, grid, anc
         o = row_broadcast(o, n_prefix, grid, anchor_stride)
         lse = row_broadcast(lse[:, None], n_prefix, grid, anchor_stride)[:, 0]
     return o, lse
+
+
+def _follower_anchor_pairs(seq_len, n_prefix, grid, anchor_stride):
+    """Follower grid tokens (y mod s != 0, ascending) and the anchor token of each,
+    (f, s*floor(y/s), x) in the same frame and column (R8, R9)."""
+    f_, h_, w_ = grid
+    s = int(anchor_stride)
+    t = np.arange(n_prefix, seq_len)
+    y = ((t - n_prefix) // w_) % h_
+    follower = t[y % s != 0]
+    anchor = follower - (y[y % s != 0] % s) * w_
+    return follower, anchor
+
+
+def repetition_cosines(q, k, n_prefix, grid, anchor_stride, scale=None, tokens=None):
+    """Cosine similarity between the attention vector of each follower token and
+    that of its anchor, for one head.
+
+    [CA-zh] S2.2A (spatial repetition detection: the cosine similarity of attention
+    vectors between different spatial rows of one frame) and [CA-fr] S2B.3 (the same
+    between the spatial rows of one image).  R10: the attention vector of token i is
+    P_i = softmax_j(s_ij) over all N keys; follower i is paired with its anchor a(i),
+    the token whose output the broadcast copies into i, and
+        cos_i = <P_i, P_a(i)> / (|P_i| |P_a(i)|).
+    tokens: optional follower tokens to evaluate (default: every follower).  Needs
+    anchor_stride >= 2 and at least one follower.  Returns (tokens, cos) in fp64.
+    """
+    q, k = _f64(q), _f64(k)
+    n = q.shape[0]
+    c = _scale(q.shape[1], scale)
+    follower, anchor = _follower_anchor_pairs(n, n_prefix, grid, anchor_stride)
+    if int(anchor_stride) < 2 or follower.size == 0:
+        raise ValueError("repetition detection needs anchor_stride >= 2 and follower rows")
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        pos = np.searchsorted(follower, tokens)
+        if np.any(pos >= follower.size) or np.any(follower[np.minimum(pos, follower.size - 1)] != tokens):
+            raise ValueError("tokens must be follower tokens")
+        follower, anchor = follower[pos], anchor[pos]
+    p_f, _ = _softmax_rows((q[follower] @ k.T) * c)
+    p_a, _ = _softmax_rows((q[anchor] @ k.T) * c)
+    cos = (p_f * p_a).sum(axis=1) / (np.sqrt((p_f * p_f).sum(axis=1)) * np.sqrt((p_a * p_a).sum(axis=1)))
+    return follower, cos
+
+
+def repetition_score(q, k, n_prefix, grid, anchor_stride, scale=None):
+    """Repetition score of one head: the mean of repetition_cosines over all its
+    follower tokens (R11).  Returns (score, cos [N] with NaN at non-followers)."""
+    n = q.shape[0]
+    tokens, cos = repetition_cosines(q, k, n_prefix, grid, anchor_stride, scale)
+    full = np.full(n, np.nan)
+    full[tokens] = cos
+    return float(cos.mean()), full
+
+
+def mark_repetition_heads(scores, gamma):
+    """Repetition flags from per-input head scores.
+
+    [CA-zh] S2.2A: a (timestep, layer, head) whose similarity exceeds gamma is marked
+    spatially repetitive; [CA-fr] S2B.3: the head is marked repetitive.  R11: scores
+    is [n_draws, heads]; each head's scores are added one at a time in fp64 in draw
+    order, divided by n_draws, and compared strictly with gamma.  Returns uint8
+    [heads].
+    """
+    scores = np.asarray(scores)
+    n_draws, heads = scores.shape
+    out = np.zeros(heads, dtype=np.uint8)
+    for h in range(heads):
+        acc = 0.0
+        for d in range(n_draws):
+            acc += float(scores[d, h])
+        out[h] = 1 if acc / n_draws > float(gamma) else 0
+    return out

@@ -136,6 +136,42 @@ def rows_wrong_anchor(seq_len, n_prefix, grid, anchor_stride, is_rep_head):
     return rows
 
 
+def pairs_previous_row(seq_len, n_prefix, grid, anchor_stride):
+    """Each follower compared with the image row just above it."""
+    follower, _ = _orig["_follower_anchor_pairs"](seq_len, n_prefix, grid, anchor_stride)
+    return follower, follower - grid[2]
+
+
+def rep_cosine_of_logits(q, k, n_prefix, grid, anchor_stride, scale=None, tokens=None):
+    """Cosine of the score rows instead of the probability rows."""
+    q, k = O._f64(q), O._f64(k)
+    c = O._scale(q.shape[1], scale)
+    follower, anchor = O._follower_anchor_pairs(q.shape[0], n_prefix, grid, anchor_stride)
+    if int(anchor_stride) < 2 or follower.size == 0:
+        raise ValueError("no followers")
+    if tokens is not None:
+        pos = np.searchsorted(follower, np.asarray(tokens))
+        follower, anchor = follower[pos], anchor[pos]
+    sf, sa = (q[follower] @ k.T) * c, (q[anchor] @ k.T) * c
+    cos = (sf * sa).sum(1) / (np.linalg.norm(sf, axis=1) * np.linalg.norm(sa, axis=1))
+    return follower, cos
+
+
+def rep_score_counts_anchors(q, k, n_prefix, grid, anchor_stride, scale=None):
+    """Anchor rows counted in the mean with similarity 1."""
+    _, full = _orig["repetition_score"](q, k, n_prefix, grid, anchor_stride, scale)
+    g = full[n_prefix:]
+    return float(np.where(np.isnan(g), 1.0, g).mean()), full
+
+
+def mark_any_draw(scores, gamma):
+    return (np.asarray(scores) > gamma).any(axis=0).astype(np.uint8)
+
+
+def mark_at_least(scores, gamma):
+    return (np.asarray(scores, dtype=np.float64).mean(axis=0) >= gamma).astype(np.uint8)
+
+
 MUTANTS = {
     "dense_no_scale": ("dense_attention", dense_no_scale),
     "dense_softmax_over_queries": ("dense_attention", dense_softmax_over_queries),
@@ -149,6 +185,11 @@ MUTANTS = {
     "sparse_masked_as_zero_logits": ("sparse_attention", sparse_masked_as_zero_logits),
     "broadcast_along_x": ("row_broadcast", broadcast_along_x),
     "rows_wrong_anchor": ("computed_rows", rows_wrong_anchor),
+    "pairs_previous_row": ("_follower_anchor_pairs", pairs_previous_row),
+    "rep_cosine_of_logits": ("repetition_cosines", rep_cosine_of_logits),
+    "rep_score_counts_anchors": ("repetition_score", rep_score_counts_anchors),
+    "mark_any_draw": ("mark_repetition_heads", mark_any_draw),
+    "mark_at_least": ("mark_repetition_heads", mark_at_least),
 }
 
 

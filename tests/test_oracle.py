@@ -351,3 +351,123 @@ def test_repetition_short_last_group():
     o = np.arange(15, dtype=np.float64)[:, None]
     out = oracle.row_broadcast(o, 0, (1, 5, 3), 4).reshape(5, 3)
     np.testing.assert_array_equal(out[:, 1], [1, 1, 1, 1, 13])
+
+
+# ---------------------------------------------------------------- repetition detection
+
+
+def _grid_pairs(n_prefix, grid, s):
+    """(follower, anchor) tokens enumerated over (f, y, x) of the token grid."""
+    f_, h_, w_ = grid
+    fol, anc = [], []
+    for f in range(f_):
+        for y in range(h_):
+            if y % s == 0:
+                continue
+            for x in range(w_):
+                fol.append(n_prefix + (f * h_ + y) * w_ + x)
+                anc.append(n_prefix + (f * h_ + (y // s) * s) * w_ + x)
+    return np.array(fol), np.array(anc)
+
+
+def test_hand_repetition_pairs():
+    g = GOLD["repetition_pairs_example"]
+    n = g["n_prefix"] + int(np.prod(g["grid"]))
+    rng = np.random.default_rng(80)
+    q, k = rng.standard_normal((n, 6)), rng.standard_normal((n, 6))
+    toks, cos = oracle.repetition_cosines(q, k, g["n_prefix"], g["grid"], g["stride"])
+    np.testing.assert_array_equal(toks, g["followers"])
+    assert np.all(cos < 1 - 1e-6)  # distinct random queries: never identical rows
+    # a follower whose query equals that of its hand-derived anchor attends identically
+    q[g["followers"]] = q[g["anchors"]]
+    _, cos = oracle.repetition_cosines(q, k, g["n_prefix"], g["grid"], g["stride"])
+    np.testing.assert_allclose(cos, 1.0, atol=1e-13)
+
+
+def test_hand_repetition_cosine():
+    g = GOLD["repetition_cosine_example"]
+    q = math.log(2.0) * np.array(g["q_units"], dtype=np.float64)
+    k = np.eye(4)
+    want = np.array(g["cos_num"]) / np.sqrt(np.array(g["cos_den_sq"], dtype=np.float64))
+    toks, cos = oracle.repetition_cosines(q, k, g["n_prefix"], g["grid"], g["stride"], scale=g["scale"])
+    np.testing.assert_array_equal(toks, g["followers"])
+    np.testing.assert_allclose(cos, want, rtol=1e-14)
+    score, full = oracle.repetition_score(q, k, g["n_prefix"], g["grid"], g["stride"], scale=g["scale"])
+    assert abs(score - want.mean()) < 1e-14
+    assert np.isnan(full[:2]).all() and np.allclose(full[2:], want, rtol=1e-14)
+
+
+def _two_level_cos(n, key_group, set_a, set_b, beta):
+    """Closed form of the cosine between two softmax rows whose logits are beta on
+    the keys of some groups and 0 elsewhere: with weight w = e^beta, the
+    unnormalised rows hold w or 1 and the normalisations cancel."""
+    in_a, in_b = set_a[key_group], set_b[key_group]
+    both = int(np.sum(in_a & in_b))
+    one = int(np.sum(in_a ^ in_b))
+    neither = n - int(np.sum(in_a | in_b))
+    w = math.exp(beta)
+    dot = both * w * w + one * w + neither
+    na = int(in_a.sum()) * w * w + (n - int(in_a.sum()))
+    nb = int(in_b.sum()) * w * w + (n - int(in_b.sum()))
+    return dot / math.sqrt(na * nb)
+
+
+@pytest.mark.parametrize("n_prefix,grid,s,seed", [(0, (2, 6, 5), 2, 81), (4, (3, 7, 4), 4, 82),
+                                                  (2, (1, 9, 3), 3, 83)])
+def test_repetition_two_level_closed_form(n_prefix, grid, s, seed):
+    n = n_prefix + int(np.prod(grid))
+    d, beta = 12, 1.7
+    rng = np.random.default_rng(seed)
+    key_group = rng.integers(0, d, n)
+    k = np.eye(d)[key_group]
+    sets = rng.random((n, d)) < 0.4
+    q = beta * sets.astype(np.float64)
+    toks, cos = oracle.repetition_cosines(q, k, n_prefix, grid, s, scale=1.0)
+    fol, anc = _grid_pairs(n_prefix, grid, s)
+    np.testing.assert_array_equal(toks, fol)
+    want = np.array([_two_level_cos(n, key_group, sets[a], sets[i], beta) for i, a in zip(fol, anc)])
+    np.testing.assert_allclose(cos, want, rtol=1e-13)
+    score, _ = oracle.repetition_score(q, k, n_prefix, grid, s, scale=1.0)
+    assert abs(score - want.mean()) < 1e-13
+    # the default scale 1/sqrt(d) is the same as beta / sqrt(d)
+    toks2, cos2 = oracle.repetition_cosines(q, k, n_prefix, grid, s)
+    want2 = [_two_level_cos(n, key_group, sets[a], sets[i], beta / math.sqrt(d)) for i, a in zip(fol, anc)]
+    np.testing.assert_allclose(cos2, want2, rtol=1e-13)
+
+
+def test_repetition_invariants():
+    n_prefix, grid, s = 3, (2, 5, 4), 2
+    n = n_prefix + 40
+    rng = np.random.default_rng(84)
+    q, k = rng.standard_normal((n, 8)), rng.standard_normal((n, 8))
+    toks, cos = oracle.repetition_cosines(q, k, n_prefix, grid, s)
+    assert np.all((cos > 0) & (cos <= 1 + 1e-15))
+    # probabilities do not change when every key is shifted by one vector (each row's
+    # logits move by a constant) or when the keys are permuted
+    _, c_shift = oracle.repetition_cosines(q, k + rng.standard_normal(8) * 3, n_prefix, grid, s)
+    np.testing.assert_allclose(c_shift, cos, rtol=1e-12)
+    _, c_perm = oracle.repetition_cosines(q, k[rng.permutation(n)], n_prefix, grid, s)
+    np.testing.assert_allclose(c_perm, cos, rtol=1e-12)
+    # equal keys: every row is uniform
+    _, c_uni = oracle.repetition_cosines(q, np.ones((n, 8)), n_prefix, grid, s)
+    np.testing.assert_allclose(c_uni, 1.0, atol=1e-14)
+    # a subset of followers gives the same values
+    pick = toks[::3]
+    t_sub, c_sub = oracle.repetition_cosines(q, k, n_prefix, grid, s, tokens=pick)
+    np.testing.assert_array_equal(t_sub, pick)
+    np.testing.assert_array_equal(c_sub, cos[::3])
+    with pytest.raises(ValueError):
+        oracle.repetition_cosines(q, k, n_prefix, grid, s, tokens=[n_prefix])  # an anchor
+    with pytest.raises(ValueError):
+        oracle.repetition_cosines(q, k, n_prefix, grid, 1)
+    with pytest.raises(ValueError):
+        oracle.repetition_cosines(q[:n_prefix + 8], k[:n_prefix + 8], n_prefix, (2, 1, 4), 2)
+
+
+def test_hand_repetition_flags():
+    g = GOLD["repetition_flag_examples"]
+    flags = oracle.mark_repetition_heads(np.array(g["scores"]), g["gamma"])
+    np.testing.assert_array_equal(flags, g["flags"])
+    assert flags.dtype == np.uint8
+    # one draw: a plain strict threshold
+    np.testing.assert_array_equal(oracle.mark_repetition_heads([[0.5, 0.25, 0.75]], 0.5), [0, 0, 1])
