@@ -12,7 +12,9 @@ from .api import (
     n_blocks,
     rep_row_broadcast,
     select_blocks_by_energy,
+    select_rep_heads,
     sparse_attn_fwd,
+    spatial_rep_similarity,
     version,
 )
 from ._lib import LIB_PATH, LibraryMissing, load as load_library
@@ -29,6 +31,8 @@ __all__ = [
     "n_blocks",
     "rep_row_broadcast",
     "select_blocks_by_energy",
+    "select_rep_heads",
     "sparse_attn_fwd",
+    "spatial_rep_similarity",
     "version",
 ]

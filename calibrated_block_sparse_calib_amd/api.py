@@ -204,5 +204,47 @@ def dense_attn_fwd(q, k, v, *, block: int = 128, scale: float = 0.0, o: Optional
     return (o, lse) if return_lse else o
 
 
+def spatial_rep_similarity(q, k, lse, anchor_stride: int, *, n_prefix: int = 0, grid=None, scale: float = 0.0,
+                           token_cos: Optional[torch.Tensor] = None, head_sim: Optional[torch.Tensor] = None):
+    """Cosine similarity between each follower token's attention row and its
+    anchor's, and its mean per (batch item, head).  lse: fp32 [batch, heads, seq_len]
+    of the same q and k (calib_block_energy or dense_attn_fwd).  Returns
+    (head_sim [batch, heads], token_cos [batch, heads, seq_len]); token_cos is only
+    written at follower tokens (a new tensor starts as NaN)."""
+    _require_gpu(q, k, lse, token_cos, head_sim)
+    _same_layout(q, k)
+    desc = make_desc(q, 128, n_prefix, grid, scale)
+    b, h, n, _ = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n) or not lse.is_contiguous():
+        raise CalibAttnError("lse must be contiguous fp32 [batch, heads, seq_len]")
+    if token_cos is None:
+        token_cos = torch.full((b, h, n), float("nan"), dtype=torch.float32, device=q.device)
+    if head_sim is None:
+        head_sim = torch.empty((b, h), dtype=torch.float32, device=q.device)
+    for t, shape in ((token_cos, (b, h, n)), (head_sim, (b, h))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise CalibAttnError("token_cos and head_sim must be contiguous fp32 of the documented shapes")
+    _check(_lib.load().spatial_rep_similarity(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), int(anchor_stride),
+                                              _ptr(token_cos), _ptr(head_sim), _stream()),
+           "spatial_rep_similarity")
+    return head_sim, token_cos
+
+
+def select_rep_heads(head_sim: torch.Tensor, gamma: float, rep_heads: Optional[torch.Tensor] = None):
+    """head_sim fp32 [draws, heads] -> uint8 [heads] on the GPU: 1 where the mean over
+    the draws is strictly above gamma."""
+    _require_gpu(head_sim, rep_heads)
+    if head_sim.dtype != torch.float32 or head_sim.dim() != 2 or not head_sim.is_contiguous():
+        raise CalibAttnError("head_sim must be contiguous fp32 [draws, heads]")
+    d, h = head_sim.shape
+    if rep_heads is None:
+        rep_heads = torch.empty(h, dtype=torch.uint8, device=head_sim.device)
+    if rep_heads.dtype != torch.uint8 or rep_heads.numel() != h:
+        raise CalibAttnError("rep_heads must be uint8 [heads]")
+    _check(_lib.load().select_rep_heads(_ptr(head_sim), d, h, float(gamma), _ptr(rep_heads), _stream()),
+           "select_rep_heads")
+    return rep_heads
+
+
 def version() -> int:
     return int(_lib.load().cba_version())

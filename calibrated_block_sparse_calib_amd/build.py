@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libcalibattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "select_csr.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "select_csr.hip", "repetition.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -17,14 +17,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int elem_bytes(int dtype) { return dtype == CBA_DTYPE_BF16 ? 2 : 4; }
 
-// Shape, stride and dtype checks shared by every attention-shaped call.
-cba_status check_desc(const cba_attn_desc* d) {
+// Shape, stride and dtype checks shared by every attention-shaped call.  A call
+// that does not use blocks (uses_block = false) ignores desc->block.
+cba_status check_desc(const cba_attn_desc* d, bool uses_block = true) {
   if (!d) return CBA_EINVAL;
   if (d->dtype != CBA_DTYPE_F32 && d->dtype != CBA_DTYPE_BF16) return CBA_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return CBA_EUNSUPPORTED;
-  if (d->block != 32 && d->block != 64 && d->block != 128) return CBA_EUNSUPPORTED;
+  if (uses_block && d->block != 32 && d->block != 64 && d->block != 128) return CBA_EUNSUPPORTED;
   if (d->batch < 1 || d->heads < 1 || d->seq_len < 1) return CBA_EINVAL;
-  if (d->n_prefix < 0 || d->n_prefix > d->seq_len || d->n_prefix % d->block != 0) return CBA_EINVAL;
+  if (d->n_prefix < 0 || d->n_prefix > d->seq_len) return CBA_EINVAL;
+  if (uses_block && d->n_prefix % d->block != 0) return CBA_EINVAL;
   if (d->grid_f < 0 || d->grid_h < 0 || d->grid_w < 0) return CBA_EINVAL;
   const int64_t grid = (int64_t)d->grid_f * d->grid_h * d->grid_w;
   if (grid != 0 && grid != (int64_t)d->seq_len - d->n_prefix) return CBA_EINVAL;
@@ -32,8 +34,10 @@ cba_status check_desc(const cba_attn_desc* d) {
   if (d->stride_n < d->head_dim || d->stride_h < 0 || d->stride_b < 0) return CBA_EINVAL;
   const int eb = elem_bytes(d->dtype);
   if ((d->stride_n * eb) % 16 || (d->stride_h * eb) % 16 || (d->stride_b * eb) % 16) return CBA_EINVAL;
-  const int64_t nb = ((int64_t)d->seq_len + d->block - 1) / d->block;
-  if ((int64_t)d->heads * nb * d->batch > INT32_MAX) return CBA_EINVAL;
+  if (uses_block) {
+    const int64_t nb = ((int64_t)d->seq_len + d->block - 1) / d->block;
+    if ((int64_t)d->heads * nb * d->batch > INT32_MAX) return CBA_EINVAL;
+  }
   if ((int64_t)d->batch * d->heads > 65535) return CBA_EINVAL;
   return CBA_OK;
 }
@@ -45,7 +49,7 @@ AttnParams make_params(const cba_attn_desc* d) {
   p.batch = d->batch;
   p.heads = d->heads;
   p.n = d->seq_len;
-  p.nb = (d->seq_len + d->block - 1) / d->block;
+  p.nb = d->block > 0 ? (d->seq_len + d->block - 1) / d->block : 0;
   p.n_rows = d->heads * p.nb;
   p.n_prefix = d->n_prefix;
   p.gf = d->grid_f;
@@ -186,6 +190,51 @@ CBA_API cba_status dense_attn_fwd(const cba_attn_desc* desc, const void* q, cons
   p.o = o;
   p.lse = lse;
   return from_hip(run_attention(p, desc, /*with_pv=*/true, reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status spatial_rep_similarity(const cba_attn_desc* desc, const void* q, const void* k,
+                                          const float* lse, int32_t anchor_stride, float* token_cos,
+                                          float* head_sim, cba_stream_t stream) {
+  cba_status st = check_desc(desc, /*uses_block=*/false);
+  if (st) return st;
+  if (check_tensor(q) || check_tensor(k)) return CBA_EINVAL;
+  for (const void* t : {(const void*)lse, (const void*)token_cos, (const void*)head_sim})
+    if (!t || (reinterpret_cast<uintptr_t>(t) & 3u)) return CBA_EINVAL;
+  if ((int64_t)desc->grid_f * desc->grid_h * desc->grid_w == 0) return CBA_EINVAL;  // needs a token grid
+  if (anchor_stride < 2 || desc->grid_h < 2) return CBA_EINVAL;                      // no follower rows
+  const AttnParams a = make_params(desc);
+  cba::RepParams p{};
+  p.q = q;
+  p.k = k;
+  p.lse = lse;
+  p.token_cos = token_cos;
+  p.head_sim = head_sim;
+  p.sb = a.sb;
+  p.sh = a.sh;
+  p.sn = a.sn;
+  p.batch = a.batch;
+  p.heads = a.heads;
+  p.n = a.n;
+  p.n_prefix = a.n_prefix;
+  p.gf = a.gf;
+  p.gh = a.gh;
+  p.gw = a.gw;
+  p.stride = anchor_stride;
+  p.c = a.c;
+  const bool bf16 = desc->dtype == CBA_DTYPE_BF16;
+  const int64_t items =
+      cba::rep_grid(p.batch, p.heads, p.gf, p.gh, p.gw, p.stride, bf16, &p.n_groups, &p.n_sub, &p.n_chunks);
+  if (items > INT32_MAX) return CBA_EINVAL;
+  return from_hip(cba::launch_rep_similarity(p, desc->head_dim, bf16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status select_rep_heads(const float* head_sim, int32_t n_draws, int32_t heads, double gamma,
+                                    uint8_t* rep_heads, cba_stream_t stream) {
+  if (!head_sim || !rep_heads || (reinterpret_cast<uintptr_t>(head_sim) & 3u)) return CBA_EINVAL;
+  if (n_draws < 1 || heads < 1 || !std::isfinite(gamma)) return CBA_EINVAL;
+  if ((int64_t)n_draws * heads > INT32_MAX) return CBA_EINVAL;
+  return from_hip(cba::launch_rep_flags(head_sim, n_draws, heads, gamma, rep_heads,
+                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
 CBA_API const char* cba_status_str(cba_status status) {

@@ -39,6 +39,37 @@ __host__ __device__ inline bool rep_head(const AttnParams& p, int h) {
   return p.has_rep && ((p.rep_bits[h >> 5] >> (h & 31)) & 1u);
 }
 
+// Spatial-repetition similarity: Q, K and the per-row log-sum-exp of one dense
+// pass, the token grid and the anchor stride; outputs per-token cosines and
+// per-head means.  n_groups, n_sub and n_chunks describe the launch grid.
+struct RepParams {
+  const void* q;
+  const void* k;
+  const float* lse;
+  float* token_cos;
+  float* head_sim;
+  int64_t sb, sh, sn;
+  int batch, heads, n;
+  int n_prefix, gf, gh, gw;
+  int stride;  // anchor stride, >= 2
+  float c;     // softmax scale * log2(e)
+  int n_groups, n_sub, n_chunks;
+};
+
+// Launch grid of the repetition-similarity kernel: (row groups that hold a
+// follower row) x (follower sub-groups of NWV - 1 rows) x (chunks of the frame x
+// column pairs), per batch item and head.  NWV = 2 waves for stride 2, else 4;
+// chunks are 32 pairs wide for bf16 and 64 for fp32.
+inline int64_t rep_grid(int batch, int heads, int gf, int gh, int gw, int stride, bool bf16, int* n_groups,
+                        int* n_sub, int* n_chunks) {
+  const int nf = stride == 2 ? 1 : 3;
+  const int cw = bf16 ? 32 : 64;
+  *n_groups = (gh - 1 + stride - 1) / stride;
+  *n_sub = (stride - 1 + nf - 1) / nf;
+  *n_chunks = (int)(((int64_t)gf * gw + cw - 1) / cw);
+  return (int64_t)batch * heads * *n_groups * *n_sub * *n_chunks;
+}
+
 // Launchers (each enqueues on `stream` and returns the launch status).
 // Attention over the key blocks listed in p.row_ptr/p.col_idx, or over every key
 // block when p.row_ptr is null (dense).  with_pv = false computes only the LSE.
@@ -52,5 +83,9 @@ hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, do
 hipError_t launch_csr(const uint8_t* mask, int n_rows, int nkb, int32_t* row_ptr, int32_t* col_idx,
                       int64_t capacity, int32_t* work_order, hipStream_t stream);
 hipError_t launch_broadcast(const AttnParams& p, int head_dim, int elem_bytes, hipStream_t stream);
+// Per-token cosines then per-head means; p.n_groups/n_sub/n_chunks from rep_grid.
+hipError_t launch_rep_similarity(const RepParams& p, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_rep_flags(const float* head_sim, int n_draws, int heads, double gamma, uint8_t* flags,
+                            hipStream_t stream);
 
 }  // namespace cba

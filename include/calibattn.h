@@ -157,6 +157,43 @@ cba_status rep_row_broadcast(const cba_attn_desc* desc, void* o, const uint8_t* 
 cba_status dense_attn_fwd(const cba_attn_desc* desc, const void* q, const void* k, const void* v,
                           void* o, float* lse, cba_stream_t stream);
 
+/* Spatial-repetition similarity of every head, from one dense pass per
+ * calibration input (zh S2.2A, spatial repetition detection: cosine similarity of
+ * the attention vectors of different spatial rows of one frame; fr S2B.3).
+ * The attention vector of token i is its row of dense attention probabilities,
+ * P_i[j] = exp(s_ij - lse_i) over all seq_len keys.  Each follower grid token
+ * i = (f, y, x), y % anchor_stride != 0, is compared with its anchor
+ * a(i) = (f, anchor_stride * floor(y / anchor_stride), x), the token whose output
+ * rep_row_broadcast copies into it:
+ *     token_cos[b, h, i] = <P_i, P_a(i)> / (|P_i| |P_a(i)|),
+ * and head_sim[b, h] is the mean of token_cos over the follower tokens of (b, h).
+ *   lse: fp32 [batch, heads, seq_len], natural log, as written for the same q and k
+ *        by calib_block_energy or dense_attn_fwd.  It only sets the scale of each
+ *        row's exponentials: the cosine does not depend on it beyond rounding.
+ *   token_cos: fp32 [batch, heads, seq_len] output, written at follower tokens
+ *        only; every other entry is left as it was.
+ *   head_sim: fp32 [batch, heads] output.  Each is a sum in a fixed order, so
+ *        repeated calls give identical bits.
+ * The batch index is the calibration input.  Needs a token grid, grid_h >= 2 and
+ * anchor_stride >= 2 (so that follower rows exist); desc->block is not used and
+ * n_prefix need not be a multiple of it.
+ * q and k as for calib_block_energy. */
+cba_status spatial_rep_similarity(const cba_attn_desc* desc, const void* q, const void* k, const float* lse,
+                                  int32_t anchor_stride, float* token_cos, float* head_sim,
+                                  cba_stream_t stream);
+
+/* Repetition flags from the per-input head similarities (zh S2.2A: a (timestep,
+ * layer, head) whose similarity exceeds gamma is marked spatially repetitive;
+ * fr S2B.3).  rep_heads[h] = 1 when the mean over the n_draws rows of
+ * head_sim[:, h], added in fp64 one draw at a time in draw order and divided by
+ * n_draws, is strictly greater than gamma; else 0.
+ *   head_sim: fp32 [n_draws, heads] (spatial_rep_similarity with batch = n_draws).
+ *   rep_heads: uint8 [heads] device output (copy it to the host for
+ *        sparse_attn_fwd and rep_row_broadcast).
+ * A bit-exact function of the head_sim bits. */
+cba_status select_rep_heads(const float* head_sim, int32_t n_draws, int32_t heads, double gamma,
+                            uint8_t* rep_heads, cba_stream_t stream);
+
 /* Static description of a status code. */
 const char* cba_status_str(cba_status status);
 

@@ -26,10 +26,11 @@ def lib():
     return _lib.load()
 
 
-def test_header_declares_the_six_calls():
+def test_header_declares_every_call():
     names = _declared_functions()
     for n in ["calib_block_energy", "select_blocks_by_energy", "build_block_csr", "sparse_attn_fwd",
-              "rep_row_broadcast", "dense_attn_fwd", "cba_status_str", "cba_version"]:
+              "rep_row_broadcast", "dense_attn_fwd", "spatial_rep_similarity", "select_rep_heads",
+              "cba_status_str", "cba_version"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -125,3 +126,29 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(_lib.LibraryMissing):
         _lib.load()
+
+
+def test_repetition_detection_rejects_bad_arguments(lib):
+    grid = dict(grid_f=1, grid_h=16, grid_w=16)
+    d = _desc(**grid)
+    ok = (FAKE, FAKE, FAKE, 4, FAKE, FAKE, None)
+    # no token grid
+    assert lib.spatial_rep_similarity(ctypes.byref(_desc()), *ok) == EINVAL
+    # stride below 2, or a single image row: no follower rows
+    assert lib.spatial_rep_similarity(ctypes.byref(d), FAKE, FAKE, FAKE, 1, FAKE, FAKE, None) == EINVAL
+    d1 = _desc(grid_f=16, grid_h=1, grid_w=16)
+    assert lib.spatial_rep_similarity(ctypes.byref(d1), *ok) == EINVAL
+    # missing or misaligned outputs / lse
+    assert lib.spatial_rep_similarity(ctypes.byref(d), FAKE, FAKE, None, 4, FAKE, FAKE, None) == EINVAL
+    assert lib.spatial_rep_similarity(ctypes.byref(d), FAKE, FAKE, FAKE, 4, None, FAKE, None) == EINVAL
+    assert lib.spatial_rep_similarity(ctypes.byref(d), FAKE, FAKE, FAKE, 4, FAKE, ctypes.c_void_p(0x10002),
+                                      None) == EINVAL
+    # unsupported head_dim; q misaligned
+    assert lib.spatial_rep_similarity(ctypes.byref(_desc(head_dim=96, **grid)), *ok) == EUNSUPPORTED
+    assert lib.spatial_rep_similarity(ctypes.byref(d), ctypes.c_void_p(0x10008), *ok[1:]) == EINVAL
+    # select_rep_heads
+    assert lib.select_rep_heads(None, 1, 4, 0.5, FAKE, None) == EINVAL
+    assert lib.select_rep_heads(FAKE, 0, 4, 0.5, FAKE, None) == EINVAL
+    assert lib.select_rep_heads(FAKE, 1, 0, 0.5, FAKE, None) == EINVAL
+    assert lib.select_rep_heads(FAKE, 1, 4, float("nan"), FAKE, None) == EINVAL
+    assert lib.select_rep_heads(FAKE, 1, 4, 0.5, None, None) == EINVAL
