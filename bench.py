@@ -11,9 +11,9 @@ resident in HBM before the timed region.
 A step is the inference path: build_block_csr (mask -> skip list and work order)
 then sparse_attn_fwd (kept blocks only, anchor rows of repetition heads, fused
 broadcast).  value = kept-block FLOPs / step time.  The other entry points
-(calib_block_energy, select_blocks_by_energy, rep_row_broadcast, dense_attn_fwd)
-are timed in the same run and reported under "rows"; dense_attn_fwd gives the
-speedup.  The fp64 CPU oracle is timed on a bounded sample of query blocks of the
+(calib_block_energy, select_blocks_by_energy, spatial_rep_similarity,
+select_rep_heads, rep_row_broadcast, dense_attn_fwd) are timed in the same run and
+reported under "rows"; dense_attn_fwd gives the speedup.  The fp64 CPU oracle is timed on a bounded sample of query blocks of the
 same workload (cpu_baseline) and its outputs are compared with the GPU's.
 
 Prints one JSON line.
@@ -67,9 +67,14 @@ def rows_per_block(cfg, is_rep):
     return np.concatenate([r, np.zeros(pad, bool)]).reshape(cfg.nb, cfg.block).sum(1).astype(np.int64)
 
 
+KERNEL_UNIT = ("attn_bf16.hip", "mfma_util.h", "cba_internal.h")  # the sparse kernel's translation unit
+
+
 def source_hash():
+    """Hash of the sources compiled into the sparse kernel: byte counters taken on
+    another version of them are not reported."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.dirname(KERNEL_SOURCE))):
+    for name in KERNEL_UNIT:
         with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -120,6 +125,33 @@ def cpu_baseline(cfg, q, k, v, mask, rep, got_o, budget_s, seed=0):
         "kind": "oracle",
         "sample": f"{done} query blocks ({done * B} rows max) of {cfg.name}, fp64 NumPy, {dt:.1f} s",
     }, {"rows_checked": int(err.shape[0]), "max_abs": float(err.max()), "mean_abs": float(err.mean())}
+
+
+def rep_rows_per_head(cfg):
+    """Query rows spatial_rep_similarity computes per head: every row of the row
+    groups that hold a follower row (anchor row plus followers)."""
+    f_, h_, w_ = cfg.grid
+    s = cfg.anchor_stride
+    groups = (h_ - 1 + s - 1) // s
+    return f_ * w_ * min(groups * s, h_)
+
+
+def rep_sampled_parity(cfg, q, k, token_cos, n_tokens=96, seed=0):
+    """Oracle cosines of sampled follower tokens (the last one always) of a few heads
+    against the GPU's token_cos."""
+    import oracle
+
+    rng = np.random.default_rng(seed)
+    f_, h_, w_ = cfg.grid
+    t = np.arange(cfg.n_prefix, cfg.seq_len)
+    fol = t[((t - cfg.n_prefix) // w_) % h_ % cfg.anchor_stride != 0]
+    errs = []
+    for h in sorted({0, cfg.heads - 1, int(rng.integers(0, cfg.heads))}):
+        pick = np.unique(np.append(rng.choice(fol, n_tokens, replace=False), fol[-1]))
+        _, ref = oracle.repetition_cosines(q[h], k[h], cfg.n_prefix, cfg.grid, cfg.anchor_stride, tokens=pick)
+        errs.append(np.abs(token_cos[h][pick].astype(np.float64) - ref))
+    err = np.concatenate(errs)
+    return {"tokens_checked": int(err.shape[0]), "max_abs": float(err.max()), "mean_abs": float(err.mean())}
 
 
 def density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S,
@@ -373,6 +405,22 @@ def main():
         rows["calib_block_energy"] = {"ms": en_ms, "draws": 1, "tflops": 1.5 * dense_flops / en_ms / 1e9}
         sel_ms = timeit(lambda: cba.select_blocks_by_energy(energy, 0.95, 0.5))
         rows["select_blocks_by_energy"] = {"ms": sel_ms, "draws": 1}
+        # repetition detection on the same draw, from the LSE of the energy pass
+        rs_head, rs_tok = cba.spatial_rep_similarity(qd, kd, lse, cfg.anchor_stride, n_prefix=cfg.n_prefix,
+                                                     grid=cfg.grid)
+        rs_ms = timeit(lambda: cba.spatial_rep_similarity(qd, kd, lse, cfg.anchor_stride, n_prefix=cfg.n_prefix,
+                                                          grid=cfg.grid, token_cos=rs_tok, head_sim=rs_head))
+        rs_flops = 2 * rep_rows_per_head(cfg) * n * cfg.head_dim * cfg.heads  # QK^T of the computed rows
+        srh_ms = timeit(lambda: cba.select_rep_heads(rs_head, 0.9))
+        hs = rs_head[0].cpu().numpy()
+        rows["spatial_rep_similarity"] = {"ms": rs_ms, "tflops": rs_flops / rs_ms / 1e9,
+                                          "rows_per_head": rep_rows_per_head(cfg), "draws": 1,
+                                          "head_sim_min": float(hs.min()), "head_sim_max": float(hs.max()),
+                                          "select_rep_heads_ms": srh_ms}
+        log(f"spatial_rep_similarity {rs_ms:.2f} ms ({rs_flops / rs_ms / 1e9:.0f} TFLOP/s), head scores "
+            f"{hs.min():.3f}..{hs.max():.3f}")
+        rep_tok_host = rs_tok[0].cpu().numpy()
+        del rs_tok
         del do, eo, energy
         if not args.no_sweep:
             rows["density_sweep"] = density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S)
@@ -387,6 +435,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(cfg, q, k, v, mask, rep, got_o, args.cpu_budget)
         log(f"cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} cores; sampled parity {parity}")
+        if "spatial_rep_similarity" in rows:
+            rows["spatial_rep_similarity"]["parity_sample"] = rep_sampled_parity(cfg, q, k, rep_tok_host)
+            log(f"spatial_rep_similarity sampled parity {rows['spatial_rep_similarity']['parity_sample']}")
 
     traffic = traffic_from_profile()
     out = {

@@ -8,7 +8,9 @@
  *   calibration (zh S2.2A, de S2A, fr S2B): per calibration input, the attention
  *     matrix is cut into B x B tiles, each tile's energy is the sum of its attention
  *     probabilities, each query block keeps the fewest highest-energy key blocks that
- *     reach a threshold, and the per-input masks are aggregated by vote;
+ *     reach a threshold, and the per-input masks are aggregated by vote; heads whose
+ *     attention rows repeat across the image rows of a frame are marked for
+ *     anchor-row computation;
  *   inference (zh S2.2B, de S2B, fr S2C): the mask becomes a skip list and a kernel
  *     computes attention over the kept blocks only; for heads marked spatially
  *     repetitive only anchor rows are computed and then broadcast in their frame.

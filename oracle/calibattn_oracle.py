@@ -23,7 +23,9 @@ Conventions shared by every function:
   * a block mask is [nqb, nkb] with 1 = kept (the summaries' "skip list" lists the
     blocks that are computed).
 
-Readings of points the pages leave open (each is repeated where it is used):
+Readings of points the pages leave open (each is repeated where it is used; R10-R16
+concern block geometry, text tokens, the scale and encodings, which the functions
+below take as parameters):
   R1 energy is the raw sum of attention probabilities over the B x B tile;
   R2 the threshold is a fraction of the query block's own total energy;
   R3 "reach" means cumulative energy >= tau * total;
@@ -35,10 +37,10 @@ Readings of points the pages leave open (each is repeated where it is used):
   R8 a "spatial row" is one image row (f, y) of W tokens; anchors are the rows with
      y mod s == 0 and each stands for rows y .. y+s-1 of its frame;
   R9 an anchor row keeps its own query block's mask; text tokens are never followers;
-  R10 the "attention vector" of a token is its row of dense attention probabilities
+  R17 the "attention vector" of a token is its row of dense attention probabilities
      (softmax over all keys), and a follower token is compared with the token that
      the broadcast copies into it: its anchor, same frame and column;
-  R11 a head's repetition score is the mean of those cosines over all follower
+  R18 a head's repetition score is the mean of those cosines over all follower
      tokens; over calibration inputs the scores are averaged (fp64, input order)
      and the head is marked when the average is strictly above gamma.
 
@@ -303,7 +305,7 @@ def repetition_cosines(q, k, n_prefix, grid, anchor_stride, scale=None, tokens=N
 
     [CA-zh] S2.2A (spatial repetition detection: the cosine similarity of attention
     vectors between different spatial rows of one frame) and [CA-fr] S2B.3 (the same
-    between the spatial rows of one image).  R10: the attention vector of token i is
+    between the spatial rows of one image).  R17: the attention vector of token i is
     P_i = softmax_j(s_ij) over all N keys; follower i is paired with its anchor a(i),
     the token whose output the broadcast copies into i, and
         cos_i = <P_i, P_a(i)> / (|P_i| |P_a(i)|).
@@ -330,7 +332,7 @@ def repetition_cosines(q, k, n_prefix, grid, anchor_stride, scale=None, tokens=N
 
 def repetition_score(q, k, n_prefix, grid, anchor_stride, scale=None):
     """Repetition score of one head: the mean of repetition_cosines over all its
-    follower tokens (R11).  Returns (score, cos [N] with NaN at non-followers)."""
+    follower tokens (R18).  Returns (score, cos [N] with NaN at non-followers)."""
     n = q.shape[0]
     tokens, cos = repetition_cosines(q, k, n_prefix, grid, anchor_stride, scale)
     full = np.full(n, np.nan)
@@ -342,7 +344,7 @@ def mark_repetition_heads(scores, gamma):
     """Repetition flags from per-input head scores.
 
     [CA-zh] S2.2A: a (timestep, layer, head) whose similarity exceeds gamma is marked
-    spatially repetitive; [CA-fr] S2B.3: the head is marked repetitive.  R11: scores
+    spatially repetitive; [CA-fr] S2B.3: the head is marked repetitive.  R18: scores
     is [n_draws, heads]; each head's scores are added one at a time in fp64 in draw
     order, divided by n_draws, and compared strictly with gamma.  Returns uint8
     [heads].

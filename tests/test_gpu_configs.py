@@ -200,3 +200,41 @@ def test_wan14_720p_sparse_dense_and_repetition():
     err = np.concatenate(errs)
     log(f"  wan14_720p dense: rows {err.shape[0]} max {err.max():.3e} mean {err.mean():.3e}")
     assert err.max() <= 1e-2 and err.mean() <= 1e-3
+
+
+@pytest.mark.parametrize("name", ["wan14_720p", "mochi"])
+def test_repetition_detection_full_size(name):
+    """spatial_rep_similarity on one full-size draw (the launch the benchmark times):
+    sampled follower tokens of a few heads against the oracle (max 1e-4), every head
+    score equal to the mean of the token values written, and the flags of
+    select_rep_heads bit-exact against the oracle's rule on the GPU's scores."""
+    cfg = get_config(name)
+    q, k, _ = make_qkv(cfg, draw=0, with_v=False)
+    qd, kd = _dev(q[None]), _dev(k[None])
+    _, lse, _ = cba.calib_block_energy(qd, kd, None, block=cfg.block, n_prefix=cfg.n_prefix, grid=cfg.grid)
+    head_sim, token_cos = cba.spatial_rep_similarity(qd, kd, lse, cfg.anchor_stride, n_prefix=cfg.n_prefix,
+                                                     grid=cfg.grid)
+    torch.cuda.synchronize()
+    hs = head_sim.cpu().numpy()
+    tc = token_cos[0].cpu().numpy()
+    f_, h_, w_ = cfg.grid
+    t = np.arange(cfg.n_prefix, cfg.seq_len)
+    fol_mask = np.zeros(cfg.seq_len, dtype=bool)
+    fol_mask[t[((t - cfg.n_prefix) // w_) % h_ % cfg.anchor_stride != 0]] = True
+    assert np.isnan(tc[:, ~fol_mask]).all() and np.isfinite(tc[:, fol_mask]).all()
+    np.testing.assert_allclose(hs[0], tc[:, fol_mask].astype(np.float64).mean(axis=1), atol=2e-7, rtol=0)
+    rng = np.random.default_rng(9)
+    fol = np.nonzero(fol_mask)[0]
+    errs = []
+    for h in sorted({0, cfg.heads - 1, int(rng.integers(0, cfg.heads))}):
+        pick = np.unique(np.concatenate([rng.choice(fol, 64, replace=False), fol[:2], fol[-2:]]))
+        _, ref = oracle.repetition_cosines(q[h], k[h], cfg.n_prefix, cfg.grid, cfg.anchor_stride, tokens=pick)
+        errs.append(np.abs(tc[h][pick].astype(np.float64) - ref))
+    err = np.concatenate(errs)
+    log(f"  {name} repetition: {err.size} tokens, max err {err.max():.2e}; head scores "
+        f"{hs.min():.3f}..{hs.max():.3f}")
+    assert err.max() <= 1e-4
+    gamma = float(np.median(hs))
+    flags = cba.select_rep_heads(head_sim, gamma)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(flags.cpu().numpy(), oracle.mark_repetition_heads(hs, gamma))
