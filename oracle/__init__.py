@@ -10,6 +10,7 @@ from .calibattn_oracle import (
     select_blocks,
     aggregate_votes,
     build_csr,
+    build_intervals,
     computed_rows,
     sparse_attention,
     row_broadcast,
@@ -27,6 +28,7 @@ __all__ = [
     "select_blocks",
     "aggregate_votes",
     "build_csr",
+    "build_intervals",
     "computed_rows",
     "sparse_attention",
     "row_broadcast",

@@ -190,6 +190,31 @@ def build_csr(mask):
     return row_ptr, col_idx, work_order
 
 
+def build_intervals(mask):
+    """Mask rows -> runs of consecutive kept key blocks, the summaries' "block
+    intervals" of the skip list.
+
+    [CA-zh] S2.2B: the mask is turned into a skip list holding only the block
+    intervals to compute.  Layout: iv_ptr[0] = 0, iv_ptr[r+1] = iv_ptr[r] + (runs of
+    row r); run j of the row starts at key block first[j] and covers count[j] >= 1
+    consecutive kept blocks; a row's runs are ascending and maximal (a skipped block
+    separates any two).  work_order is that of build_csr (kept blocks descending,
+    ties by ascending row).  mask: [rows, nkb].  Returns (iv_ptr, first, count,
+    work_order).
+    """
+    mask = np.asarray(mask).astype(bool)
+    rows, nkb = mask.shape
+    edge = np.zeros((rows, nkb + 1), dtype=np.int8)
+    edge[:, :nkb] += mask
+    edge[:, 1:] -= mask  # +1 where a run starts, -1 just past where one ends
+    r_start, c_start = np.nonzero(edge == 1)
+    _, c_end = np.nonzero(edge == -1)  # row-major scans: the ends pair with the starts in order
+    iv_ptr = np.zeros(rows + 1, dtype=np.int32)
+    iv_ptr[1:] = np.cumsum(np.bincount(r_start, minlength=rows))
+    _, _, work_order = build_csr(mask)
+    return iv_ptr, c_start.astype(np.int32), (c_end - c_start).astype(np.int32), work_order
+
+
 def computed_rows(seq_len, n_prefix, grid, anchor_stride, is_rep_head):
     """Query rows that attention computes: all rows for a normal head; for a spatial
     repetition head the text rows and the anchor rows (R8).

@@ -172,6 +172,18 @@ def mark_at_least(scores, gamma):
     return (np.asarray(scores, dtype=np.float64).mean(axis=0) >= gamma).astype(np.uint8)
 
 
+def intervals_unmerged(mask):
+    """Every kept block its own run."""
+    row_ptr, col_idx, order = _orig["build_csr"](mask)
+    return row_ptr, col_idx, np.ones_like(col_idx), order
+
+
+def intervals_inclusive_end(mask):
+    """Run length taken as (last - first + 1) of an exclusive end."""
+    iv_ptr, first, count, order = _orig["build_intervals"](mask)
+    return iv_ptr, first, count + 1, order
+
+
 MUTANTS = {
     "dense_no_scale": ("dense_attention", dense_no_scale),
     "dense_softmax_over_queries": ("dense_attention", dense_softmax_over_queries),
@@ -190,6 +202,8 @@ MUTANTS = {
     "rep_score_counts_anchors": ("repetition_score", rep_score_counts_anchors),
     "mark_any_draw": ("mark_repetition_heads", mark_any_draw),
     "mark_at_least": ("mark_repetition_heads", mark_at_least),
+    "intervals_unmerged": ("build_intervals", intervals_unmerged),
+    "intervals_inclusive_end": ("build_intervals", intervals_inclusive_end),
 }
 
 

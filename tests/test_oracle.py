@@ -106,6 +106,15 @@ def test_hand_csr_case():
     np.testing.assert_array_equal(order, g["work_order"])
 
 
+def test_hand_interval_case():
+    g = GOLD["interval_example"]
+    iv_ptr, first, count, order = oracle.build_intervals(np.array(g["mask"], dtype=np.uint8))
+    np.testing.assert_array_equal(iv_ptr, g["iv_ptr"])
+    np.testing.assert_array_equal(first, g["first"])
+    np.testing.assert_array_equal(count, g["count"])
+    np.testing.assert_array_equal(order, g["work_order"])
+
+
 def test_hand_broadcast_case():
     g = GOLD["broadcast_example"]
     n = g["n_prefix"] + int(np.prod(g["grid"]))
@@ -471,3 +480,37 @@ def test_hand_repetition_flags():
     assert flags.dtype == np.uint8
     # one draw: a plain strict threshold
     np.testing.assert_array_equal(oracle.mark_repetition_heads([[0.5, 0.25, 0.75]], 0.5), [0, 0, 1])
+
+
+# ---------------------------------------------------------------- interval skip lists
+
+
+@pytest.mark.parametrize("rows,nkb,density,seed", [(7, 1, 0.5, 90), (30, 13, 0.0, 91), (30, 13, 1.0, 92),
+                                                   (50, 40, 0.3, 93), (20, 64, 0.8, 94)])
+def test_intervals_round_trip_maximal_and_counted(rows, nkb, density, seed):
+    m = np.random.default_rng(seed).random((rows, nkb)) < density
+    iv_ptr, first, count, order = oracle.build_intervals(m)
+    assert iv_ptr[0] == 0 and np.all(np.diff(iv_ptr) >= 0)
+    back = np.zeros_like(m)
+    for r in range(rows):
+        runs = list(zip(first[iv_ptr[r]:iv_ptr[r + 1]], count[iv_ptr[r]:iv_ptr[r + 1]]))
+        for (f0, c0), (f1, _) in zip(runs, runs[1:]):
+            assert f1 > f0 + c0  # ascending, and a skipped block between two runs
+        for f0, c0 in runs:
+            assert c0 >= 1 and f0 + c0 <= nkb
+            back[r, f0:f0 + c0] = True
+        # brute force: one run per kept block whose left neighbour is skipped
+        starts = sum(1 for c in range(nkb) if m[r, c] and (c == 0 or not m[r, c - 1]))
+        assert len(runs) == starts
+    np.testing.assert_array_equal(back, m)
+    np.testing.assert_array_equal(order, oracle.build_csr(m)[2])
+
+
+def test_intervals_of_a_band_are_few():
+    # a band of width 5 around the diagonal is one run per row
+    nkb = 20
+    m = np.abs(np.arange(nkb)[:, None] - np.arange(nkb)[None, :]) <= 2
+    iv_ptr, first, count, _ = oracle.build_intervals(m)
+    np.testing.assert_array_equal(np.diff(iv_ptr), 1)
+    np.testing.assert_array_equal(first, np.maximum(np.arange(nkb) - 2, 0))
+    np.testing.assert_array_equal(count, m.sum(axis=1))
