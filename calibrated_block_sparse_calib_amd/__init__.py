@@ -6,6 +6,7 @@ loaded on first use; a missing library raises instead of falling back.
 from .api import (
     CalibAttnError,
     build_block_csr,
+    build_block_intervals,
     calib_block_energy,
     dense_attn_fwd,
     make_desc,
@@ -14,6 +15,7 @@ from .api import (
     select_blocks_by_energy,
     select_rep_heads,
     sparse_attn_fwd,
+    sparse_attn_fwd_intervals,
     spatial_rep_similarity,
     version,
 )
@@ -24,6 +26,7 @@ __all__ = [
     "LibraryMissing",
     "LIB_PATH",
     "build_block_csr",
+    "build_block_intervals",
     "calib_block_energy",
     "dense_attn_fwd",
     "load_library",
@@ -33,6 +36,7 @@ __all__ = [
     "select_blocks_by_energy",
     "select_rep_heads",
     "sparse_attn_fwd",
+    "sparse_attn_fwd_intervals",
     "spatial_rep_similarity",
     "version",
 ]

@@ -41,6 +41,9 @@ SIGNATURES = {
     "rep_row_broadcast": (c_i32, [_PD, c_p, c_p, c_i32, c_p]),
     "dense_attn_fwd": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p, c_p]),
     "spatial_rep_similarity": (c_i32, [_PD, c_p, c_p, c_p, c_i32, c_p, c_p, c_p]),
+    "build_block_intervals": (c_i32, [c_p, c_i32, c_i32, c_p, c_p, c_i64, c_p]),
+    "sparse_attn_fwd_intervals": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p, c_i32, c_i32, c_p, c_p,
+                                          c_p]),
     "select_rep_heads": (c_i32, [c_p, c_i32, c_i32, c_f64, c_p, c_p]),
     "cba_status_str": (ctypes.c_char_p, [c_i32]),
     "cba_version": (c_i32, []),

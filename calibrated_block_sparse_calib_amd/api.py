@@ -148,6 +148,62 @@ def build_block_csr(mask: torch.Tensor, with_order: bool = True, exact: bool = F
     return row_ptr, col_idx, order
 
 
+def build_block_intervals(mask: torch.Tensor, exact: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mask uint8 [..., nkb] (rows = all leading dims) -> (iv_ptr int32 [rows + 1],
+    ivs [capacity]): the maximal runs of kept blocks of every row, each packed as
+    first | count << 16 (uint32 bits, held in an int32 tensor).
+
+    exact=False: one call with the capacity that can never be exceeded (rows *
+    ceil(nkb / 2)); the first iv_ptr[-1] entries are the runs.  exact=True: a count
+    pass, a host read of the total, then the fill into exactly that many entries."""
+    _require_gpu(mask)
+    if mask.dtype != torch.uint8 or not mask.is_contiguous():
+        raise CalibAttnError("mask must be contiguous uint8")
+    nkb = mask.shape[-1]
+    rows = mask.numel() // nkb
+    lib = _lib.load()
+    iv_ptr = torch.empty(rows + 1, dtype=torch.int32, device=mask.device)
+    if exact:
+        _check(lib.build_block_intervals(_ptr(mask), rows, nkb, _ptr(iv_ptr), None, 0, _stream()),
+               "build_block_intervals(count)")
+        cap = int(iv_ptr[-1].item())
+    else:
+        cap = rows * ((nkb + 1) // 2)
+    ivs = torch.empty(max(cap, 1), dtype=torch.int32, device=mask.device)
+    _check(lib.build_block_intervals(_ptr(mask), rows, nkb, _ptr(iv_ptr), _ptr(ivs), cap, _stream()),
+           "build_block_intervals")
+    return iv_ptr, ivs
+
+
+def sparse_attn_fwd_intervals(q, k, v, iv_ptr, ivs, *, block: int, work_order=None, rep_heads=None,
+                              anchor_stride: int = 1, fuse_broadcast: bool = True, n_prefix: int = 0, grid=None,
+                              scale: float = 0.0, o: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """sparse_attn_fwd with the skip list as block intervals (build_block_intervals)."""
+    _require_gpu(q, k, v, iv_ptr, ivs, work_order, o, lse)
+    if o is None:
+        o = torch.empty_like(q)
+    _same_layout(q, k, v, o)
+    desc = make_desc(q, block, n_prefix, grid, scale)
+    b, h, n, _ = q.shape
+    if return_lse and lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if iv_ptr.dtype != torch.int32 or ivs.dtype not in (torch.int32, torch.uint32):
+        raise CalibAttnError("iv_ptr must be int32 and ivs 32-bit")
+    if iv_ptr.numel() != h * n_blocks(n, block) + 1:
+        raise CalibAttnError("iv_ptr must have heads * nb + 1 entries")
+    if work_order is not None and (work_order.dtype != torch.int32 or work_order.numel() != h * n_blocks(n, block)):
+        raise CalibAttnError("work_order must be int32 [heads * nb]")
+    rep_arr, rep_ptr = _rep_array(rep_heads, h)
+    _check(_lib.load().sparse_attn_fwd_intervals(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(iv_ptr),
+                                                 _ptr(ivs), ivs.numel(), _ptr(work_order), rep_ptr,
+                                                 int(anchor_stride), int(bool(fuse_broadcast)), _ptr(o), _ptr(lse),
+                                                 _stream()),
+           "sparse_attn_fwd_intervals")
+    del rep_arr
+    return (o, lse) if return_lse else o
+
+
 def sparse_attn_fwd(q, k, v, row_ptr, col_idx, *, block: int, work_order=None, rep_heads=None,
                     anchor_stride: int = 1, fuse_broadcast: bool = True, n_prefix: int = 0, grid=None,
                     scale: float = 0.0, o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,

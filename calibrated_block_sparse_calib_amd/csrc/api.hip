@@ -165,6 +165,40 @@ CBA_API cba_status sparse_attn_fwd(const cba_attn_desc* desc, const void* q, con
   return from_hip(run_attention(p, desc, /*with_pv=*/true, reinterpret_cast<hipStream_t>(stream)));
 }
 
+CBA_API cba_status build_block_intervals(const uint8_t* mask, int32_t n_rows, int32_t nkb, int32_t* iv_ptr,
+                                         uint32_t* ivs, int64_t iv_capacity, cba_stream_t stream) {
+  if (!mask || !iv_ptr || n_rows < 1 || nkb < 1 || nkb > 65535) return CBA_EINVAL;
+  if ((int64_t)n_rows * nkb > INT32_MAX) return CBA_EINVAL;  // run counts must fit int32
+  if (ivs && iv_capacity < 0) return CBA_EINVAL;
+  return from_hip(cba::launch_intervals(mask, n_rows, nkb, iv_ptr, ivs, ivs ? iv_capacity : 0,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status sparse_attn_fwd_intervals(const cba_attn_desc* desc, const void* q, const void* k,
+                                             const void* v, const int32_t* iv_ptr, const uint32_t* ivs,
+                                             int64_t iv_len, const int32_t* work_order, const uint8_t* rep_heads,
+                                             int32_t anchor_stride, int32_t fuse_broadcast, void* o, float* lse,
+                                             cba_stream_t stream) {
+  cba_status st = check_desc(desc);
+  if (st) return st;
+  if (check_tensor(q) || check_tensor(k) || check_tensor(v) || check_tensor(o)) return CBA_EINVAL;
+  if (!iv_ptr || iv_len < 0 || (iv_len > 0 && !ivs)) return CBA_EINVAL;
+  AttnParams p = make_params(desc);
+  if ((st = set_rep(p, desc, rep_heads, anchor_stride))) return st;
+  static const uint32_t kNoRuns = 0;  // a non-null list for iv_len == 0 (never read)
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.row_ptr = iv_ptr;
+  p.ivs = iv_len > 0 ? ivs : &kNoRuns;
+  p.col_len = iv_len;
+  p.work_order = work_order;
+  p.fuse_broadcast = fuse_broadcast != 0;
+  return from_hip(run_attention(p, desc, /*with_pv=*/true, reinterpret_cast<hipStream_t>(stream)));
+}
+
 CBA_API cba_status rep_row_broadcast(const cba_attn_desc* desc, void* o, const uint8_t* rep_heads,
                                      int32_t anchor_stride, cba_stream_t stream) {
   cba_status st = check_desc(desc);

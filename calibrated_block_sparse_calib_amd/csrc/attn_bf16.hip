@@ -47,7 +47,9 @@ struct Cfg {
 // The four tile buffers are separate LDS objects, so the compiler can tell that
 // the reads of one buffer never alias the asynchronous loads into another and
 // does not wait for those loads before reading.
-template <int D, int B, bool PV, bool LSE, bool BUF>
+// IV: the skip list is given as runs of consecutive blocks (p.ivs) instead of
+// block indices (p.col_idx).
+template <int D, int B, bool PV, bool LSE, bool BUF, bool IV>
 __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, bfraw* k0s, bfraw* k1s,
                                           bfraw* v0s, bfraw* v1s, int* rowlist, int* wcnt) {
   using C = Cfg<D, B>;
@@ -93,13 +95,39 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
   // Uniform across the wave: the skip-list reads become scalar loads.
   beg = __builtin_amdgcn_readfirstlane(beg);
   nblk = __builtin_amdgcn_readfirstlane(nblk);
-  const int nsteps = nblk * C::SPB;
   // The skip list is read-only for the kernel's lifetime: reading it through the
   // constant address space lets the (uniform) reads go to the scalar unit.
   const __attribute__((address_space(4))) int32_t* cidx =
       (const __attribute__((address_space(4))) int32_t*)p.col_idx;
+  const __attribute__((address_space(4))) uint32_t* civ =
+      (const __attribute__((address_space(4))) uint32_t*)p.ivs;
+  // Runs: [beg, beg + nblk) indexes the row's runs; the blocks to visit are the
+  // sum of their counts.  A cursor (run iv_j, offset iv_off) hands out the blocks
+  // in order, one per call of step_key0 with s % SPB == 0 (its calls come in
+  // increasing s).
+  const int iv_end = beg + nblk;
+  int iv_j = beg, iv_off = 0, iv_kb = -1;
+  if (IV) {
+    int tot = 0;
+    for (int j = beg; j < iv_end; ++j) tot += (int)(civ[j] >> 16);
+    nblk = tot;
+  }
+  const int nsteps = nblk * C::SPB;
   auto step_key0 = [&](int s) -> int {
-    const int kb = dense ? s / C::SPB : cidx[beg + s / C::SPB];
+    int kb;
+    if (IV) {
+      if (s % C::SPB == 0) {
+        while (iv_j < iv_end && iv_off >= (int)(civ[iv_j] >> 16)) {
+          ++iv_j;
+          iv_off = 0;
+        }
+        iv_kb = iv_j < iv_end ? (int)(civ[iv_j] & 0xffffu) + iv_off : -1;
+        ++iv_off;
+      }
+      kb = iv_kb;
+    } else {
+      kb = dense ? s / C::SPB : cidx[beg + s / C::SPB];
+    }
     if (kb < 0 || kb >= p.nb) return -1;
     const int k0 = kb * B + (s % C::SPB) * C::KT;
     return k0 < p.n ? k0 : -1;
@@ -287,7 +315,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
 
 // One workgroup per item: item i = blockIdx.x is row work_order[i / batch] (or
 // row i / batch when there is no order) and batch item i % batch.
-template <int D, int B, bool PV, bool LSE, bool BUF>
+template <int D, int B, bool PV, bool LSE, bool BUF, bool IV>
 __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParams p) {
   using C = Cfg<D, B>;
   __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
@@ -296,7 +324,7 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
   __shared__ int wcnt[4];
   const int it = blockIdx.x / p.batch, b = blockIdx.x - it * p.batch;
   const int row = p.work_order ? p.work_order[it] : it;
-  attn_item<D, B, PV, LSE, BUF>(p, row, b, k0s, k1s, v0s, v1s, rowlist, wcnt);
+  attn_item<D, B, PV, LSE, BUF, IV>(p, row, b, k0s, k1s, v0s, v1s, rowlist, wcnt);
 }
 
 // Block energy, sweep 2: E[qb, kb] = sum over the tile of exp(s_ij - lse_i), with
@@ -417,12 +445,15 @@ hipError_t launch_attn_t(const AttnParams& p, bool with_pv, hipStream_t stream) 
   // addressable with them.
   const bool buf = (int64_t)(p.n + C::KT) * p.sn * 2 < ((int64_t)1 << 31);
   void (*kern)(AttnParams);
-  if (!with_pv) {
-    kern = buf ? attn_bf16_kernel<D, B, false, true, true> : attn_bf16_kernel<D, B, false, true, false>;
+  if (p.ivs) {  // interval skip list (with_pv only)
+    if (p.lse) kern = buf ? attn_bf16_kernel<D, B, true, true, true, true> : attn_bf16_kernel<D, B, true, true, false, true>;
+    else kern = buf ? attn_bf16_kernel<D, B, true, false, true, true> : attn_bf16_kernel<D, B, true, false, false, true>;
+  } else if (!with_pv) {
+    kern = buf ? attn_bf16_kernel<D, B, false, true, true, false> : attn_bf16_kernel<D, B, false, true, false, false>;
   } else if (p.lse) {
-    kern = buf ? attn_bf16_kernel<D, B, true, true, true> : attn_bf16_kernel<D, B, true, true, false>;
+    kern = buf ? attn_bf16_kernel<D, B, true, true, true, false> : attn_bf16_kernel<D, B, true, true, false, false>;
   } else {
-    kern = buf ? attn_bf16_kernel<D, B, true, false, true> : attn_bf16_kernel<D, B, true, false, false>;
+    kern = buf ? attn_bf16_kernel<D, B, true, false, true, false> : attn_bf16_kernel<D, B, true, false, false, false>;
   }
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -74,8 +74,26 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(AttnParams p) {
     const int64_t end = min((int64_t)p.row_ptr[row + 1], p.col_len);
     nblk = (int)max((int64_t)0, end - beg);
   }
-  for (int bi = 0; bi < nblk; ++bi) {
-    const int kb = dense ? bi : p.col_idx[beg + bi];
+  // Interval skip list: [beg, beg + nblk) are runs (first | count << 16); a cursor
+  // (run iv_j, offset iv_off) walks their blocks in order.
+  const int iv_end = beg + nblk;
+  int iv_j = beg, iv_off = 0, total = nblk;
+  if (p.ivs) {
+    total = 0;
+    for (int j = beg; j < iv_end; ++j) total += (int)(p.ivs[j] >> 16);
+  }
+  for (int bi = 0; bi < total; ++bi) {
+    int kb;
+    if (p.ivs) {
+      while (iv_j < iv_end && iv_off >= (int)(p.ivs[iv_j] >> 16)) {
+        ++iv_j;
+        iv_off = 0;
+      }
+      kb = iv_j < iv_end ? (int)(p.ivs[iv_j] & 0xffffu) + iv_off : -1;
+      ++iv_off;
+    } else {
+      kb = dense ? bi : p.col_idx[beg + bi];
+    }
     if (kb < 0 || kb >= p.nb) continue;
     for (int sub = 0; sub < B / TK; ++sub) {
       const int k0 = kb * B + sub * TK;

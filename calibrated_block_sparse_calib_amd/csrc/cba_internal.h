@@ -24,9 +24,10 @@ struct AttnParams {
   int batch, heads, n, nb;
   int n_prefix, gf, gh, gw;
   float c;  // softmax scale * log2(e): scores are handled in base-2 units
-  const int32_t* row_ptr;
+  const int32_t* row_ptr;   // skip list: row offsets into col_idx, or into ivs
   const int32_t* col_idx;
-  int64_t col_len;
+  const uint32_t* ivs;      // non-null: runs (first | count << 16) instead of col_idx
+  int64_t col_len;          // valid entries of col_idx or ivs
   const int32_t* work_order;
   int n_rows;      // heads * nb
   int anchor_stride;
@@ -82,6 +83,8 @@ hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, do
                          hipStream_t stream);
 hipError_t launch_csr(const uint8_t* mask, int n_rows, int nkb, int32_t* row_ptr, int32_t* col_idx,
                       int64_t capacity, int32_t* work_order, hipStream_t stream);
+hipError_t launch_intervals(const uint8_t* mask, int n_rows, int nkb, int32_t* iv_ptr, uint32_t* ivs,
+                            int64_t capacity, hipStream_t stream);
 hipError_t launch_broadcast(const AttnParams& p, int head_dim, int elem_bytes, hipStream_t stream);
 // Per-token cosines then per-head means; p.n_groups/n_sub/n_chunks from rep_grid.
 hipError_t launch_rep_similarity(const RepParams& p, int head_dim, bool bf16, hipStream_t stream);

@@ -238,6 +238,69 @@ __global__ __launch_bounds__(kOrderThreads) void csr_order_kernel(int n_rows, co
   }
 }
 
+// ---------------------------------------------------------------- intervals
+//
+// Runs of consecutive kept blocks, one packed word per run: first block in the
+// low 16 bits, block count in the high 16 bits.  One wave per row walks the row
+// 64 blocks at a time with ballots.  In a chunk with kept bits K (bit l = block
+// j0 + l), a run starts at l when K has l and not l - 1 (the bit before the chunk
+// comes from the previous chunk), and ends at l when K has l and not l + 1 (the bit
+// after the chunk comes from the next chunk).  A run ending at l began at the
+// highest start at or below l in the chunk, or, if there is none, in an earlier
+// chunk (the run still open when the chunk began).
+// count: runs per row into iv_ptr[r + 1]; the CSR scan then makes them offsets;
+// fill:  each end lane writes its run at its rank among the row's runs.
+
+__device__ inline uint64_t chunk_bits(const uint8_t* m, int nkb, int j0) {
+  const int j = j0 + (threadIdx.x & 63);
+  return __ballot(j < nkb && m[j] != 0);
+}
+
+__global__ __launch_bounds__(64 * kWaves) void iv_count_kernel(const uint8_t* mask, int n_rows, int nkb,
+                                                              int32_t* iv_ptr) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (blockIdx.x == 0 && threadIdx.x == 0) iv_ptr[0] = 0;
+  if (row >= n_rows) return;
+  const uint8_t* m = mask + (int64_t)row * nkb;
+  uint64_t carry = 0;
+  int cnt = 0;
+  for (int j0 = 0; j0 < nkb; j0 += 64) {
+    const uint64_t k = chunk_bits(m, nkb, j0);
+    cnt += __popcll(k & ~((k << 1) | carry));
+    carry = k >> 63;
+  }
+  if (lane == 0) iv_ptr[row + 1] = cnt;
+}
+
+__global__ __launch_bounds__(64 * kWaves) void iv_fill_kernel(const uint8_t* mask, int n_rows, int nkb,
+                                                             const int32_t* iv_ptr, uint32_t* ivs,
+                                                             int64_t capacity) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const uint8_t* m = mask + (int64_t)row * nkb;
+  int64_t pos0 = iv_ptr[row];
+  uint64_t carry = 0;
+  int open_first = 0;  // first block of the run open at the start of the chunk
+  uint64_t k = chunk_bits(m, nkb, 0);
+  for (int j0 = 0; j0 < nkb; j0 += 64) {
+    const uint64_t k_next = j0 + 64 < nkb ? chunk_bits(m, nkb, j0 + 64) : 0;
+    const uint64_t starts = k & ~((k << 1) | carry);
+    const uint64_t ends = k & ~((k >> 1) | (k_next << 63));
+    if ((ends >> lane) & 1) {
+      const uint64_t s_le = starts & ((2ull << lane) - 1ull);  // starts at or below this lane
+      const int first = s_le ? j0 + 63 - __clzll(s_le) : open_first;
+      const int64_t pos = pos0 + __popcll(ends & ((1ull << lane) - 1ull));
+      if (pos < capacity) ivs[pos] = (uint32_t)first | ((uint32_t)(j0 + lane - first + 1) << 16);
+    }
+    pos0 += __popcll(ends);
+    if (starts) open_first = j0 + 63 - __clzll(starts);  // only used while a run stays open
+    carry = k >> 63;
+    k = k_next;
+  }
+}
+
 // ---------------------------------------------------------------- broadcast
 //
 // One workgroup per (image row (f, y), batch * head).  Follower rows of repetition
@@ -295,6 +358,22 @@ hipError_t launch_csr(const uint8_t* mask, int n_rows, int nkb, int32_t* row_ptr
   if (work_order) {
     hipLaunchKernelGGL(csr_order_kernel, dim3((unsigned)(nkb + 1)), dim3(kOrderThreads), 0, stream, n_rows,
                        (const int32_t*)row_ptr, work_order);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_intervals(const uint8_t* mask, int n_rows, int nkb, int32_t* iv_ptr, uint32_t* ivs,
+                            int64_t capacity, hipStream_t stream) {
+  const dim3 rows_grid((unsigned)((n_rows + kWaves - 1) / kWaves));
+  hipLaunchKernelGGL(iv_count_kernel, rows_grid, dim3(64 * kWaves), 0, stream, mask, n_rows, nkb, iv_ptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, n_rows, iv_ptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ivs) {
+    hipLaunchKernelGGL(iv_fill_kernel, rows_grid, dim3(64 * kWaves), 0, stream, mask, n_rows, nkb,
+                       (const int32_t*)iv_ptr, ivs, capacity);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

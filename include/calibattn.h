@@ -120,6 +120,25 @@ cba_status build_block_csr(const uint8_t* mask, int32_t n_rows, int32_t nkb, int
                            int32_t* col_idx, int64_t col_idx_capacity, int32_t* work_order,
                            cba_stream_t stream);
 
+/* Skip list as block intervals (zh S2.2B: the mask becomes a skip list holding
+ * only the block intervals to compute): the maximal runs of consecutive kept
+ * blocks of each mask row.  A compact form of the skip list for the per
+ * (timestep, layer, head) mask dictionary: a banded mask row is a few runs where
+ * its CSR row holds every block.
+ *   mask: uint8 [n_rows, nkb] (1 = kept), nkb <= 65535.
+ *   iv_ptr: int32 [n_rows + 1], iv_ptr[0] = 0, iv_ptr[r+1] - iv_ptr[r] = runs of
+ *           row r.  Always written.
+ *   ivs: uint32 [iv_capacity] or NULL (count pass only).  Run j of row r is
+ *           ivs[iv_ptr[r] + j] = first | (count << 16): blocks first .. first +
+ *           count - 1 are kept, count >= 1; a row's runs are ascending and a
+ *           skipped block separates any two.  Entries at or beyond iv_capacity are
+ *           not written (iv_ptr[n_rows] > iv_capacity tells the caller); a capacity
+ *           of n_rows * ceil(nkb / 2) can never be exceeded.
+ * For the longest-first row order, call build_block_csr with col_idx = NULL.
+ * Integer results, bit-exact. */
+cba_status build_block_intervals(const uint8_t* mask, int32_t n_rows, int32_t nkb, int32_t* iv_ptr,
+                                 uint32_t* ivs, int64_t iv_capacity, cba_stream_t stream);
+
 /* Exact attention over the kept key blocks only (zh S2.2B; de S2B; fr S2C).
  * For query token i in query block qb of head h, o_i = sum_j softmax_j(s_ij) v_j
  * with s_ij = scale * q_i . k_j and j over the tokens of the key blocks listed for
@@ -145,6 +164,18 @@ cba_status sparse_attn_fwd(const cba_attn_desc* desc, const void* q, const void*
                            const int32_t* work_order, const uint8_t* rep_heads,
                            int32_t anchor_stride, int32_t fuse_broadcast, void* o, float* lse,
                            cba_stream_t stream);
+
+/* sparse_attn_fwd with the skip list given as block intervals (zh S2.2B), as
+ * written by build_block_intervals for a [heads, nb, nb] mask: row r = h * nb + qb
+ * visits the blocks of runs ivs[iv_ptr[r] .. iv_ptr[r+1]) in order.  iv_len =
+ * number of valid ivs entries (positions at or beyond it are ignored; blocks
+ * outside [0, nb) are skipped).  Every other argument and every result as in
+ * sparse_attn_fwd; the same mask gives bit-identical outputs through either
+ * call. */
+cba_status sparse_attn_fwd_intervals(const cba_attn_desc* desc, const void* q, const void* k, const void* v,
+                                     const int32_t* iv_ptr, const uint32_t* ivs, int64_t iv_len,
+                                     const int32_t* work_order, const uint8_t* rep_heads, int32_t anchor_stride,
+                                     int32_t fuse_broadcast, void* o, float* lse, cba_stream_t stream);
 
 /* Anchor-row broadcast for spatial repetition heads (zh S2.1; fr S2C):
  * O[b, h, f, y, x] <- O[b, h, f, anchor_stride * floor(y / anchor_stride), x] for

@@ -30,6 +30,7 @@ def test_header_declares_every_call():
     names = _declared_functions()
     for n in ["calib_block_energy", "select_blocks_by_energy", "build_block_csr", "sparse_attn_fwd",
               "rep_row_broadcast", "dense_attn_fwd", "spatial_rep_similarity", "select_rep_heads",
+              "build_block_intervals", "sparse_attn_fwd_intervals",
               "cba_status_str", "cba_version"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -152,3 +153,21 @@ def test_repetition_detection_rejects_bad_arguments(lib):
     assert lib.select_rep_heads(FAKE, 1, 0, 0.5, FAKE, None) == EINVAL
     assert lib.select_rep_heads(FAKE, 1, 4, float("nan"), FAKE, None) == EINVAL
     assert lib.select_rep_heads(FAKE, 1, 4, 0.5, None, None) == EINVAL
+
+
+def test_intervals_reject_bad_arguments(lib):
+    assert lib.build_block_intervals(None, 4, 4, FAKE, None, 0, None) == EINVAL
+    assert lib.build_block_intervals(FAKE, 0, 4, FAKE, None, 0, None) == EINVAL
+    assert lib.build_block_intervals(FAKE, 4, 70000, FAKE, None, 0, None) == EINVAL  # runs need 16-bit blocks
+    assert lib.build_block_intervals(FAKE, 4, 4, None, None, 0, None) == EINVAL
+    assert lib.build_block_intervals(FAKE, 4, 4, FAKE, FAKE, -1, None) == EINVAL
+    d = _desc()
+    # no iv_ptr; negative length; a length without runs
+    assert lib.sparse_attn_fwd_intervals(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, 4, None, None, 1, 0, FAKE,
+                                         None, None) == EINVAL
+    assert lib.sparse_attn_fwd_intervals(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, -1, None, None, 1, 0, FAKE,
+                                         None, None) == EINVAL
+    assert lib.sparse_attn_fwd_intervals(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 4, None, None, 1, 0, FAKE,
+                                         None, None) == EINVAL
+    assert lib.sparse_attn_fwd_intervals(ctypes.byref(_desc(block=48)), FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None,
+                                         1, 0, FAKE, None, None) == EUNSUPPORTED

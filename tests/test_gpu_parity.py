@@ -296,15 +296,18 @@ def test_wide_row_stride_takes_global_load_path():
     kwargs = dict(block=128, rep_heads=rep, anchor_stride=4, grid=cfg.grid)
     o_c, l_c = cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, return_lse=True, **kwargs)
     o_w, l_w = cba.sparse_attn_fwd(qw, kw, vw, row_ptr, col_idx, o=ow, return_lse=True, **kwargs)
+    iv_ptr, ivs = cba.build_block_intervals(torch.from_numpy(mask).cuda())
+    o_wi = cba.sparse_attn_fwd_intervals(qw, kw, vw, iv_ptr, ivs, o=wide(torch.zeros_like(qd)), **kwargs)
     e_c, le_c, _ = cba.calib_block_energy(qd, kd, None, block=128)
     e_w, le_w, _ = cba.calib_block_energy(qw, kw, None, block=128)
     d_c = cba.dense_attn_fwd(qd, kd, vd, block=128)
     d_w = cba.dense_attn_fwd(qw, kw, vw, block=128, o=wide(torch.zeros_like(qd)))
     torch.cuda.synchronize()
     assert torch.equal(o_c, o_w.contiguous()) and torch.equal(l_c, l_w)
+    assert torch.equal(o_c, o_wi.contiguous())
     assert torch.equal(e_c, e_w) and torch.equal(le_c, le_w)
     assert torch.equal(d_c, d_w.contiguous())
     ref_o, _ = _oracle_sparse(cfg, q, k, v, mask, rep, 4)
     assert_close_out(to_host(o_w)[0], ref_o, "bf16", "wide-stride sparse O")
-    del qw, kw, vw, ow
+    del qw, kw, vw, ow, o_wi
     torch.cuda.empty_cache()
