@@ -127,6 +127,11 @@ def cpu_baseline(cfg, q, k, v, mask, rep, got_o, budget_s, seed=0):
     }, {"rows_checked": int(err.shape[0]), "max_abs": float(err.max()), "mean_abs": float(err.mean())}
 
 
+def skip_list_bytes(rows, nkb, nnz, runs):
+    """Storage of one (timestep, layer) mask entry: bitmask, CSR, block intervals."""
+    return {"bitmask": rows * ((nkb + 7) // 8), "csr": 4 * (rows + 1 + nnz), "intervals": 4 * (rows + 1 + runs)}
+
+
 def rep_rows_per_head(cfg):
     """Query rows spatial_rep_similarity computes per head: every row of the row
     groups that hold a follower row (anchor row plus followers)."""
@@ -194,11 +199,13 @@ def density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S
             "marginal_tflops": 1e-9 / slope}
 
 
-def calibrated_workload(name, reps=2):
+def calibrated_workload(name, reps=2, tau_schedule=None):
     """One calibrated workload end to end: calib_block_energy over every draw
     (LSE-only dense sweep + energy sweep), select_blocks_by_energy, build_block_csr
-    and sparse_attn_fwd on a held-out draw, plus dense_attn_fwd for the speedup.
-    Per timestep bucket when the workload has several."""
+    and sparse_attn_fwd on a held-out draw, the same through block intervals, plus
+    dense_attn_fwd for the speedup.  Per timestep bucket when the workload has
+    several; tau_schedule gives each bucket its own energy threshold (early
+    buckets first), else every bucket uses the workload's tau."""
     import torch
 
     import calibrated_block_sparse_calib_amd as cba
@@ -238,26 +245,39 @@ def calibrated_workload(name, reps=2):
         e_ms = timed(lambda: cba.calib_block_energy(qc, kc, None, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid,
                                                    lse=lse, energy=energy))
         cal_flops = 4 * n * n * d * H * cfg.calib_draws  # QK^T in both sweeps
-        mask = cba.select_blocks_by_energy(energy, cfg.tau, cfg.rho, True, cfg.n_prefix_blocks)
-        s_ms = timed(lambda: cba.select_blocks_by_energy(energy, cfg.tau, cfg.rho, True, cfg.n_prefix_blocks,
+        tau = cfg.tau if tau_schedule is None else tau_schedule[min(bucket, len(tau_schedule) - 1)]
+        mask = cba.select_blocks_by_energy(energy, tau, cfg.rho, True, cfg.n_prefix_blocks)
+        s_ms = timed(lambda: cba.select_blocks_by_energy(energy, tau, cfg.rho, True, cfg.n_prefix_blocks,
                                                         mask=mask))
         row_ptr, col_idx, _ = cba.build_block_csr(mask, with_order=False)
         c_ms = timed(lambda: cba.build_block_csr(mask, with_order=False))
         o = torch.empty_like(qd)
         sp_ms = timed(lambda: cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, block=B, n_prefix=cfg.n_prefix,
                                                   grid=cfg.grid, o=o))
+        iv_ptr, ivs = cba.build_block_intervals(mask)
+        ivb_ms = timed(lambda: cba.build_block_intervals(mask))
+        o_iv = torch.empty_like(qd)
+        iv_ms = timed(lambda: cba.sparse_attn_fwd_intervals(qd, kd, vd, iv_ptr, ivs, block=B, n_prefix=cfg.n_prefix,
+                                                            grid=cfg.grid, o=o_iv))
+        same = bool(torch.equal(o, o_iv))
+        n_runs = int(iv_ptr[-1].item())
+        del o_iv, iv_ptr, ivs
         de_ms = timed(lambda: cba.dense_attn_fwd(qd, kd, vd, block=B, o=o))
         m = mask.cpu().numpy()
         kept = kept_flops(m, cfg, np.zeros(H, bool), (rows_per_block(cfg, False),) * 2)
         dens = m.mean(axis=(1, 2))
-        res.update({"bucket": bucket, "draws": cfg.calib_draws, "calib_ms": e_ms,
+        res.update({"bucket": bucket, "tau": tau, "draws": cfg.calib_draws, "calib_ms": e_ms,
                     "calib_tflops": cal_flops / e_ms / 1e9, "select_ms": s_ms, "csr_ms": c_ms,
                     "mask_density": float(m.mean()), "head_density_min": float(dens.min()),
                     "head_density_max": float(dens.max()), "sparse_ms": sp_ms, "sparse_tflops": kept / sp_ms / 1e9,
-                    "dense_ms": de_ms, "speedup_vs_dense": de_ms / sp_ms})
+                    "dense_ms": de_ms, "speedup_vs_dense": de_ms / sp_ms,
+                    "intervals_build_ms": ivb_ms, "sparse_intervals_ms": iv_ms, "intervals_same_output": same,
+                    "runs": n_runs, "kept_blocks": int(m.sum()),
+                    "skip_list_bytes": skip_list_bytes(H * cfg.nb, cfg.nb, int(m.sum()), n_runs)})
         log(f"{name} bucket {bucket}: calibration {e_ms:.1f} ms ({res['calib_tflops']:.0f} TFLOP/s), select "
             f"{s_ms:.2f} ms, density {res['mask_density']:.3f}, sparse {sp_ms:.2f} ms "
-            f"({res['sparse_tflops']:.0f} TFLOP/s kept), dense {de_ms:.2f} ms")
+            f"({res['sparse_tflops']:.0f} TFLOP/s kept), dense {de_ms:.2f} ms; intervals: {n_runs} runs for "
+            f"{int(m.sum())} blocks, sparse {iv_ms:.2f} ms")
         out.append(res)
         del qc, kc, qd, kd, vd, energy, lse, mask, row_ptr, col_idx, o
         torch.cuda.empty_cache()
@@ -280,6 +300,9 @@ def main():
     ap.add_argument("--calibrated", default="",
                     help="comma-separated calibrated workloads (wan13_480p, mochi, hunyuan, or 'all') to also time "
                          "end to end: calibration over all draws, selection, skip list, sparse attention")
+    ap.add_argument("--tau-schedule", default="",
+                    help="comma-separated energy thresholds, one per timestep bucket of the calibrated workloads "
+                         "(early buckets first); default: each workload's own tau")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -398,6 +421,20 @@ def main():
         rows["rep_row_broadcast"] = {"ms": bc_ms, "algorithmic_bytes": bc_bytes, "gbs": bc_bytes / bc_ms / 1e6}
         unfused_ms = timeit(lambda: sparse(fuse=0))
         rows["sparse_attn_fwd_unfused"] = {"ms": unfused_ms}
+        # the same mask as block intervals (runs of kept blocks): build, then attention through the runs
+        iv_ptr, ivs = cba.build_block_intervals(md)
+        ivb_ms = timeit(lambda: cba.build_block_intervals(md))
+        iv_o = torch.empty_like(qd)
+        iv_ms = timeit(lambda: cba.sparse_attn_fwd_intervals(qd, kd, vd, iv_ptr, ivs, block=B, rep_heads=rep,
+                                                             anchor_stride=cfg.anchor_stride, n_prefix=cfg.n_prefix,
+                                                             grid=cfg.grid, o=iv_o))
+        n_runs = int(iv_ptr[-1].item())
+        rows["build_block_intervals"] = {"ms": ivb_ms, "runs": n_runs,
+                                         "algorithmic_bytes": int(2 * mask.size + 4 * (iv_ptr.numel() + n_runs))}
+        rows["sparse_attn_fwd_intervals"] = {"ms": iv_ms, "tflops": flops / iv_ms / 1e9,
+                                             "same_output_as_csr": bool(torch.equal(iv_o, od))}
+        rows["skip_list_bytes"] = skip_list_bytes(cfg.heads * nb, nb, int(mask.sum()), n_runs)
+        del iv_o, iv_ptr, ivs
         energy = torch.empty((1, cfg.heads, nb, nb), dtype=torch.float32, device="cuda")
         lse = torch.empty((1, cfg.heads, n), dtype=torch.float32, device="cuda")
         eo = torch.empty_like(qd)
@@ -429,7 +466,8 @@ def main():
         names = ["wan13_480p", "mochi", "hunyuan"] if args.calibrated == "all" else args.calibrated.split(",")
         del qd, kd, vd, od, md, row_ptr, col_idx, order
         torch.cuda.empty_cache()
-        rows["calibrated"] = {name: calibrated_workload(name) for name in names}
+        sched = [float(x) for x in args.tau_schedule.split(",")] if args.tau_schedule else None
+        rows["calibrated"] = {name: calibrated_workload(name, tau_schedule=sched) for name in names}
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
@@ -458,7 +496,7 @@ def main():
                    "rep_heads": int(rep.sum()), "anchor_stride": cfg.anchor_stride,
                    "schedule": args.order},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "speedup_vs_dense": round(rows["dense_attn_fwd"]["ms"] / wall_ms, 3) if rows else None,
+        "speedup_vs_dense": round(rows["dense_attn_fwd"]["ms"] / wall_ms, 3) if "dense_attn_fwd" in rows else None,
         "roofline": {"bound": "mfma", "kernel": "sparse_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
