@@ -6,6 +6,7 @@ this package.  The GPU library never calls it and shares no code with it.
 from .calibattn_oracle import (
     dense_attention,
     block_energy,
+    block_energy_from_lse,
     select_row,
     select_blocks,
     aggregate_votes,
@@ -24,6 +25,7 @@ from .calibattn_oracle import (
 __all__ = [
     "dense_attention",
     "block_energy",
+    "block_energy_from_lse",
     "select_row",
     "select_blocks",
     "aggregate_votes",

@@ -42,7 +42,9 @@ below take as parameters):
      the broadcast copies into it: its anchor, same frame and column;
   R18 a head's repetition score is the mean of those cosines over all follower
      tokens; over calibration inputs the scores are averaged (fp64, input order)
-     and the head is marked when the average is strictly above gamma.
+     and the head is marked when the average is strictly above gamma;
+  R22 a later search reuses the LSE cached by an earlier one as it is (no
+     correction): each row's energy terms are then scaled by one factor per row.
 
 Parity pins: every function is pinned by tests against library routines, closed
 forms, invariants or brute force (tests/test_oracle.py).
@@ -107,6 +109,31 @@ def block_energy(q, k, block, scale=None, q_blocks=None):
     return out
 
 
+def block_energy_from_lse(q, k, lse, block, scale=None, q_blocks=None):
+    """Block energy from a given log-sum-exp: E[qb, kb] = sum over i in qb and j in kb
+    of exp(s_ij - lse_i).
+
+    [AdaSpa] S2: the search pass caches the LSE of the dense attention it computes,
+    and later searches reuse that cache instead of recomputing it; [CA-zh] S2.2A for
+    the tile energy.  With the LSE of the same q and k this is block_energy; with an
+    LSE cached from another input (an earlier denoising step) each row's terms are
+    that row's probabilities times exp(lse_true_i - lse_i) (R22).  lse: [N], natural
+    log.  Returns fp64 [nqb, nkb], or the rows listed in q_blocks.
+    """
+    q, k, lse = _f64(q), _f64(k), _f64(lse)
+    n = q.shape[0]
+    c = _scale(q.shape[1], scale)
+    nb = (n + block - 1) // block
+    starts = np.arange(0, n, block)
+    rows = range(nb) if q_blocks is None else q_blocks
+    out = np.zeros((len(rows), nb), dtype=np.float64)
+    for r, qb in enumerate(rows):
+        lo, hi = qb * block, min(n, (qb + 1) * block)
+        w = np.exp((q[lo:hi] @ k.T) * c - lse[lo:hi, None])
+        out[r] = np.add.reduceat(w.sum(axis=0), starts)
+    return out
+
+
 def select_row(e, tau):
     """Fewest key blocks, highest energy first, whose cumulative energy reaches
     tau times the row total.
@@ -149,16 +176,18 @@ def select_blocks(energy, tau, rho=0.5, force_diag=True, n_dense_prefix_blocks=0
 
     energy: [draws, heads, nqb, nkb]. Per draw and row: select_row; then votes over
     draws and aggregate_votes; then R7 forcing (diagonal; rows and columns of the
-    first n_dense_prefix_blocks blocks).  Returns (mask uint8 [heads, nqb, nkb],
-    votes int32 [heads, nqb, nkb]).
+    first n_dense_prefix_blocks blocks).  tau is one threshold, or one per head (the
+    per-head recall targets of [AdaSpa] S2, head-adaptive sparsity).  Returns
+    (mask uint8 [heads, nqb, nkb], votes int32 [heads, nqb, nkb]).
     """
     energy = _f64(energy)
     n_draws, heads, nqb, nkb = energy.shape
+    taus = np.broadcast_to(np.asarray(tau, dtype=np.float64), (heads,))
     votes = np.zeros((heads, nqb, nkb), dtype=np.int32)
     for d in range(n_draws):
         for h in range(heads):
             for qb in range(nqb):
-                votes[h, qb] += select_row(energy[d, h, qb], tau)
+                votes[h, qb] += select_row(energy[d, h, qb], taus[h])
     mask = aggregate_votes(votes, n_draws, rho)
     if force_diag:
         idx = np.arange(min(nqb, nkb))

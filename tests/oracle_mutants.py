@@ -184,6 +184,16 @@ def intervals_inclusive_end(mask):
     return iv_ptr, first, count + 1, order
 
 
+def energy_from_lse_recomputed(q, k, lse, block, scale=None, q_blocks=None):
+    """Ignores the given LSE and renormalises each row."""
+    return _orig["block_energy"](q, k, block, scale, q_blocks)
+
+
+def select_first_head_tau(energy, tau, rho=0.5, force_diag=True, n_dense_prefix_blocks=0):
+    """Uses the first head's threshold for every head."""
+    return _orig["select_blocks"](energy, np.ravel(np.asarray(tau))[0], rho, force_diag, n_dense_prefix_blocks)
+
+
 MUTANTS = {
     "dense_no_scale": ("dense_attention", dense_no_scale),
     "dense_softmax_over_queries": ("dense_attention", dense_softmax_over_queries),
@@ -204,6 +214,8 @@ MUTANTS = {
     "mark_at_least": ("mark_repetition_heads", mark_at_least),
     "intervals_unmerged": ("build_intervals", intervals_unmerged),
     "intervals_inclusive_end": ("build_intervals", intervals_inclusive_end),
+    "energy_from_lse_recomputed": ("block_energy_from_lse", energy_from_lse_recomputed),
+    "select_first_head_tau": ("select_blocks", select_first_head_tau),
 }
 
 

@@ -514,3 +514,53 @@ def test_intervals_of_a_band_are_few():
     np.testing.assert_array_equal(np.diff(iv_ptr), 1)
     np.testing.assert_array_equal(first, np.maximum(np.arange(nkb) - 2, 0))
     np.testing.assert_array_equal(count, m.sum(axis=1))
+
+
+# ---------------------------------------------------------------- online search pieces
+
+
+def test_hand_cached_lse_energy():
+    g = GOLD["cached_lse_example"]
+    h = GOLD["softmax_example"]
+    q = np.array(h["q"])[:, None]
+    k = np.log(np.array(h["k_exp"]))[:, None]
+    lse = np.full(4, math.log(g["lse_uniform_exp"]))
+    np.testing.assert_allclose(oracle.block_energy_from_lse(q, k, lse, h["block"], scale=h["scale"]),
+                               g["energy_uniform"], rtol=1e-14)
+    lse = np.log(np.array(g["lse_rows_exp"]))
+    np.testing.assert_allclose(oracle.block_energy_from_lse(q, k, lse, h["block"], scale=h["scale"]),
+                               g["energy_rows"], rtol=1e-14)
+
+
+@pytest.mark.parametrize("n,block", [(96, 32), (77, 16)])
+def test_energy_from_lse_against_block_energy(n, block):
+    rng = np.random.default_rng(n)
+    q, k, v = rng.standard_normal((n, 8)), rng.standard_normal((n, 8)), rng.standard_normal((n, 8))
+    _, lse = oracle.dense_attention(q, k, v)
+    ref = oracle.block_energy(q, k, block)
+    np.testing.assert_allclose(oracle.block_energy_from_lse(q, k, lse, block), ref, rtol=1e-12)
+    # a common shift scales every energy by exp(-shift)
+    np.testing.assert_allclose(oracle.block_energy_from_lse(q, k, lse + 0.7, block), ref * math.exp(-0.7),
+                               rtol=1e-12)
+    # per-row shifts: each query block's total is the sum of its rows' exp(-shift)
+    delta = rng.uniform(-1, 1, n)
+    e = oracle.block_energy_from_lse(q, k, lse + delta, block)
+    totals = [np.exp(-delta[qb * block:(qb + 1) * block]).sum() for qb in range(e.shape[0])]
+    np.testing.assert_allclose(e.sum(axis=1), totals, rtol=1e-12)
+    sub = oracle.block_energy_from_lse(q, k, lse, block, q_blocks=[1, 0])
+    np.testing.assert_array_equal(sub, oracle.block_energy_from_lse(q, k, lse, block)[[1, 0]])
+
+
+def test_hand_per_head_tau_selection():
+    g = GOLD["per_head_tau_example"]
+    e = np.array(g["e"], dtype=np.float64)
+    energy = np.stack([e, e])[None, :, None, :]  # [draws 1, heads 2, rows 1, nkb]
+    mask, _ = oracle.select_blocks(energy, g["tau"], rho=0.5, force_diag=False)
+    np.testing.assert_array_equal(mask[:, 0], g["keep"])
+    # equal per-head thresholds are the scalar threshold
+    rng = np.random.default_rng(5)
+    en = rng.random((3, 4, 6, 6))
+    a, va = oracle.select_blocks(en, [0.8] * 4, 0.5)
+    b, vb = oracle.select_blocks(en, 0.8, 0.5)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(va, vb)
