@@ -5,6 +5,7 @@ loaded on first use; a missing library raises instead of falling back.
 """
 from .api import (
     CalibAttnError,
+    block_energy_from_lse,
     build_block_csr,
     build_block_intervals,
     calib_block_energy,
@@ -13,6 +14,7 @@ from .api import (
     n_blocks,
     rep_row_broadcast,
     select_blocks_by_energy,
+    select_blocks_by_energy_heads,
     select_rep_heads,
     sparse_attn_fwd,
     sparse_attn_fwd_intervals,
@@ -25,6 +27,7 @@ __all__ = [
     "CalibAttnError",
     "LibraryMissing",
     "LIB_PATH",
+    "block_energy_from_lse",
     "build_block_csr",
     "build_block_intervals",
     "calib_block_energy",
@@ -34,6 +37,7 @@ __all__ = [
     "n_blocks",
     "rep_row_broadcast",
     "select_blocks_by_energy",
+    "select_blocks_by_energy_heads",
     "select_rep_heads",
     "sparse_attn_fwd",
     "sparse_attn_fwd_intervals",

@@ -121,6 +121,51 @@ def select_blocks_by_energy(energy: torch.Tensor, tau: float, rho: float = 0.5, 
     return (mask, votes) if return_votes else mask
 
 
+def block_energy_from_lse(q, k, lse, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,
+                          energy: Optional[torch.Tensor] = None):
+    """Energy sweep alone from a given (possibly cached) LSE fp32 [batch, heads, seq_len].
+    Returns energy fp32 [batch, heads, nb, nb]."""
+    _require_gpu(q, k, lse, energy)
+    _same_layout(q, k)
+    desc = make_desc(q, block, n_prefix, grid, scale)
+    b, h, n, _ = q.shape
+    nb = n_blocks(n, block)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n) or not lse.is_contiguous():
+        raise CalibAttnError("lse must be contiguous fp32 [batch, heads, seq_len]")
+    if energy is None:
+        energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
+    if not energy.is_contiguous() or energy.numel() != b * h * nb * nb:
+        raise CalibAttnError("energy must be contiguous fp32 [batch, heads, nb, nb]")
+    _check(_lib.load().block_energy_from_lse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(energy),
+                                             _stream()), "block_energy_from_lse")
+    return energy
+
+
+def select_blocks_by_energy_heads(energy: torch.Tensor, tau_heads, rho: float = 0.5, force_diag: bool = True,
+                                  n_dense_prefix_blocks: int = 0, mask: Optional[torch.Tensor] = None,
+                                  votes: Optional[torch.Tensor] = None, return_votes: bool = False):
+    """select_blocks_by_energy with one threshold per head (tau_heads: a sequence of
+    heads floats, kept on the host)."""
+    _require_gpu(energy)
+    if energy.dtype != torch.float32 or energy.dim() != 4 or not energy.is_contiguous():
+        raise CalibAttnError("energy must be contiguous fp32 [draws, heads, nb, nb]")
+    d, h, nb, nb2 = energy.shape
+    if nb != nb2:
+        raise CalibAttnError("energy must be square per head")
+    taus = np.ascontiguousarray(np.asarray(tau_heads, dtype=np.float64).reshape(-1))
+    if taus.shape[0] != h:
+        raise CalibAttnError("tau_heads needs one threshold per head")
+    if mask is None:
+        mask = torch.empty((h, nb, nb), dtype=torch.uint8, device=energy.device)
+    if return_votes and votes is None:
+        votes = torch.empty((h, nb, nb), dtype=torch.int32, device=energy.device)
+    _check(_lib.load().select_blocks_by_energy_heads(_ptr(energy), d, h, nb, taus.ctypes.data_as(ctypes.c_void_p),
+                                                     float(rho), int(bool(force_diag)), int(n_dense_prefix_blocks),
+                                                     _ptr(mask), _ptr(votes), _stream()),
+           "select_blocks_by_energy_heads")
+    return (mask, votes) if return_votes else mask
+
+
 def build_block_csr(mask: torch.Tensor, with_order: bool = True, exact: bool = False,
                     ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
     """mask uint8 [..., nkb] (rows = all leading dims) -> (row_ptr, col_idx, work_order).

@@ -128,8 +128,43 @@ CBA_API cba_status select_blocks_by_energy(const float* energy, int32_t n_draws,
   if ((int64_t)heads * nb > INT32_MAX) return CBA_EINVAL;
   if (!std::isfinite(tau) || !std::isfinite(rho) || tau < 0.0) return CBA_EINVAL;
   if (n_dense_prefix_blocks < 0 || n_dense_prefix_blocks > nb) return CBA_EINVAL;
-  return from_hip(cba::launch_select(energy, n_draws, heads, nb, tau, rho, force_diag != 0, n_dense_prefix_blocks,
+  cba::TauTable taus{};
+  taus.t[0] = tau;
+  return from_hip(cba::launch_select(energy, n_draws, heads, nb, taus, rho, force_diag != 0, n_dense_prefix_blocks,
                                      mask, votes, reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status select_blocks_by_energy_heads(const float* energy, int32_t n_draws, int32_t heads, int32_t nb,
+                                                 const double* tau_heads, double rho, int32_t force_diag,
+                                                 int32_t n_dense_prefix_blocks, uint8_t* mask, int32_t* votes,
+                                                 cba_stream_t stream) {
+  if (!energy || !mask || !tau_heads) return CBA_EINVAL;
+  if (n_draws < 1 || heads < 1 || heads > cba::kMaxTauHeads || nb < 1 || nb > 4096) return CBA_EINVAL;
+  if (!std::isfinite(rho) || n_dense_prefix_blocks < 0 || n_dense_prefix_blocks > nb) return CBA_EINVAL;
+  cba::TauTable taus{};
+  taus.per_head = 1;
+  for (int h = 0; h < heads; ++h) {
+    if (!std::isfinite(tau_heads[h]) || tau_heads[h] < 0.0) return CBA_EINVAL;
+    taus.t[h] = tau_heads[h];
+  }
+  return from_hip(cba::launch_select(energy, n_draws, heads, nb, taus, rho, force_diag != 0, n_dense_prefix_blocks,
+                                     mask, votes, reinterpret_cast<hipStream_t>(stream)));
+}
+
+CBA_API cba_status block_energy_from_lse(const cba_attn_desc* desc, const void* q, const void* k, const float* lse,
+                                         float* energy, cba_stream_t stream) {
+  cba_status st = check_desc(desc);
+  if (st) return st;
+  if (check_tensor(q) || check_tensor(k) || !lse || !energy) return CBA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(energy) & 3u)) return CBA_EINVAL;
+  AttnParams p = make_params(desc);
+  p.q = q;
+  p.k = k;
+  p.lse = const_cast<float*>(lse);  // read only by the energy sweep
+  p.energy = energy;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(desc->dtype == CBA_DTYPE_BF16 ? cba::launch_energy_bf16(p, desc->head_dim, desc->block, s)
+                                                : cba::launch_energy_f32(p, desc->head_dim, desc->block, s));
 }
 
 CBA_API cba_status build_block_csr(const uint8_t* mask, int32_t n_rows, int32_t nkb, int32_t* row_ptr,

@@ -40,6 +40,14 @@ __host__ __device__ inline bool rep_head(const AttnParams& p, int h) {
   return p.has_rep && ((p.rep_bits[h >> 5] >> (h & 31)) & 1u);
 }
 
+// Energy thresholds of the block selection, passed by value to the kernel: one
+// for every head (per_head = 0: t[0]) or one per head.
+constexpr int kMaxTauHeads = 256;
+struct TauTable {
+  double t[kMaxTauHeads];
+  int per_head;
+};
+
 // Spatial-repetition similarity: Q, K and the per-row log-sum-exp of one dense
 // pass, the token grid and the anchor stride; outputs per-token cosines and
 // per-head means.  n_groups, n_sub and n_chunks describe the launch grid.
@@ -78,7 +86,7 @@ hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block, bool w
 hipError_t launch_energy_bf16(const AttnParams& p, int head_dim, int block, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, int block, bool with_pv, hipStream_t stream);
 hipError_t launch_energy_f32(const AttnParams& p, int head_dim, int block, hipStream_t stream);
-hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, double tau, double rho,
+hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, const TauTable& taus, double rho,
                          int force_diag, int n_prefix_blocks, uint8_t* mask, int32_t* votes,
                          hipStream_t stream);
 hipError_t launch_csr(const uint8_t* mask, int n_rows, int nkb, int32_t* row_ptr, int32_t* col_idx,

@@ -25,7 +25,7 @@ __device__ inline uint32_t sortable_desc(float f) {
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* energy, int n_draws, int heads,
-                                                             int nb, double tau, double rho, int force_diag,
+                                                             int nb, TauTable taus, double rho, int force_diag,
                                                              int n_prefix_blocks, uint8_t* mask,
                                                              int32_t* votes_out) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -40,6 +40,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* energy
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int h = row / nb, qb = row - h * nb;
+  const double tau = taus.per_head ? taus.t[h] : taus.t[0];
   for (int j = tid; j < nb; j += kSelThreads) vote[j] = (tau >= 1.0) ? n_draws : 0;
 
   if (tau < 1.0) {
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256) void broadcast_kernel(AttnParams p, int row_by
 
 }  // namespace
 
-hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, double tau, double rho,
+hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, const TauTable& taus, double rho,
                          int force_diag, int n_prefix_blocks, uint8_t* mask, int32_t* votes,
                          hipStream_t stream) {
   int p2 = 1;
@@ -338,7 +339,7 @@ hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, do
                                      (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)((int64_t)heads * nb)), dim3(kSelThreads), lds, stream,
-                     energy, n_draws, heads, nb, tau, rho, force_diag, n_prefix_blocks, mask, votes);
+                     energy, n_draws, heads, nb, taus, rho, force_diag, n_prefix_blocks, mask, votes);
   return hipGetLastError();
 }
 

@@ -85,6 +85,18 @@ cba_status calib_block_energy(const cba_attn_desc* desc, const void* q, const vo
                               const void* v, void* o, float* lse, float* energy,
                               cba_stream_t stream);
 
+/* Block energy sweep alone, from a given log-sum-exp ([AdaSpa] S2: the search pass
+ * caches the LSE of its dense pass and later searches reuse that cache; zh S2.2A
+ * for the tile energy).  energy[b, h, qb, kb] = sum over i in qb and j in kb of
+ * exp(s_ij - lse[b, h, i]).  With the LSE of the same q and k (calib_block_energy,
+ * dense_attn_fwd) this is calib_block_energy's sweep 2, bit for bit; with an LSE
+ * cached from an earlier input each row's terms carry one factor per row.
+ *   lse: fp32 [batch, heads, seq_len], natural log (read only).
+ *   energy: fp32 [batch, heads, nb, nb] output; every entry written, each the sum of
+ *           one tile in a fixed order. */
+cba_status block_energy_from_lse(const cba_attn_desc* desc, const void* q, const void* k, const float* lse,
+                                 float* energy, cba_stream_t stream);
+
 /* Calibrated block mask from per-draw energies (zh S2.2A; de S2A.2-3; fr S2B.1-2).
  *   energy: fp32 [n_draws, heads, nb, nb] (as written by calib_block_energy).
  *   Per draw and row, key blocks are ordered by (energy descending, index
@@ -101,6 +113,16 @@ cba_status select_blocks_by_energy(const float* energy, int32_t n_draws, int32_t
                                    double tau, double rho, int32_t force_diag,
                                    int32_t n_dense_prefix_blocks, uint8_t* mask, int32_t* votes,
                                    cba_stream_t stream);
+
+/* select_blocks_by_energy with one energy threshold per head (the per-head recall
+ * targets of head-adaptive sparsity, [AdaSpa] S2): row (h, qb) keeps the fewest
+ * blocks reaching tau_heads[h] of its energy; everything else as in
+ * select_blocks_by_energy.  tau_heads (host): double [heads], each finite and
+ * >= 0; heads <= 256. */
+cba_status select_blocks_by_energy_heads(const float* energy, int32_t n_draws, int32_t heads, int32_t nb,
+                                         const double* tau_heads, double rho, int32_t force_diag,
+                                         int32_t n_dense_prefix_blocks, uint8_t* mask, int32_t* votes,
+                                         cba_stream_t stream);
 
 /* Skip list of a block mask in CSR form (zh S2.2B; pt S2A.5; fr S2C).
  *   mask: uint8 [n_rows, nkb] (1 = kept); for attention, n_rows = heads * nb and

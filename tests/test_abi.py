@@ -30,7 +30,8 @@ def test_header_declares_every_call():
     names = _declared_functions()
     for n in ["calib_block_energy", "select_blocks_by_energy", "build_block_csr", "sparse_attn_fwd",
               "rep_row_broadcast", "dense_attn_fwd", "spatial_rep_similarity", "select_rep_heads",
-              "build_block_intervals", "sparse_attn_fwd_intervals",
+              "build_block_intervals", "sparse_attn_fwd_intervals", "block_energy_from_lse",
+              "select_blocks_by_energy_heads",
               "cba_status_str", "cba_version"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -171,3 +172,21 @@ def test_intervals_reject_bad_arguments(lib):
                                          None, None) == EINVAL
     assert lib.sparse_attn_fwd_intervals(ctypes.byref(_desc(block=48)), FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None,
                                          1, 0, FAKE, None, None) == EUNSUPPORTED
+
+
+def test_online_search_calls_reject_bad_arguments(lib):
+    d = _desc()
+    assert lib.block_energy_from_lse(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == EINVAL
+    assert lib.block_energy_from_lse(ctypes.byref(d), FAKE, FAKE, FAKE, None, None) == EINVAL
+    assert lib.block_energy_from_lse(ctypes.byref(d), None, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.block_energy_from_lse(ctypes.byref(_desc(head_dim=80)), FAKE, FAKE, FAKE, FAKE, None) == EUNSUPPORTED
+    taus = (ctypes.c_double * 2)(0.9, 0.8)
+    bad = (ctypes.c_double * 2)(0.9, float("nan"))
+    neg = (ctypes.c_double * 2)(0.9, -0.1)
+    f = lib.select_blocks_by_energy_heads
+    assert f(FAKE, 1, 2, 8, None, 0.5, 1, 0, FAKE, None, None) == EINVAL
+    assert f(FAKE, 1, 2, 8, bad, 0.5, 1, 0, FAKE, None, None) == EINVAL
+    assert f(FAKE, 1, 2, 8, neg, 0.5, 1, 0, FAKE, None, None) == EINVAL
+    assert f(FAKE, 1, 300, 8, taus, 0.5, 1, 0, FAKE, None, None) == EINVAL  # beyond 256 heads
+    assert f(FAKE, 1, 2, 5000, taus, 0.5, 1, 0, FAKE, None, None) == EINVAL
+    assert f(None, 1, 2, 8, taus, 0.5, 1, 0, FAKE, None, None) == EINVAL
