@@ -284,6 +284,91 @@ def calibrated_workload(name, reps=2, tau_schedule=None):
     return out if len(out) > 1 else out[0]
 
 
+def online_search(name, n_steps=8, search_steps=(0, 4)):
+    """Online search on one workload (the search-and-reuse schedule of AdaSpa's
+    method): at step 0 a fused dense pass gives the step's output and caches the LSE,
+    then energies, selection and the skip list; the following steps reuse the mask
+    with sparse attention; at each later search step the output comes from the
+    current mask and the energies from an LSE without a dense pass: either the one
+    cached at step 0 (the pages' reuse of the cache), or the LSE that the step's own
+    sparse pass writes over its kept blocks.  Each step's input is a fresh seeded
+    draw of the workload.  Reports per-step times against dense attention, the output
+    error against dense at every step, and the mask agreement of each later search
+    with a search from the step's own dense LSE."""
+    import torch
+
+    import calibrated_block_sparse_calib_amd as cba
+    from workloads import get_config, make_qkv
+
+    cfg = get_config(name)
+    B, H = cfg.block, cfg.heads
+    taus = [cfg.tau] * H
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    kw = dict(block=B, n_prefix=cfg.n_prefix, grid=cfg.grid)
+    t0 = time.perf_counter()
+    inputs = []
+    for st in range(n_steps):
+        q, k, v = make_qkv(cfg, draw=st)
+        inputs.append((dev(q[None]), dev(k[None]), dev(v[None])))
+    log(f"online search {name}: {n_steps} steps of inputs in {time.perf_counter() - t0:.1f} s")
+    o = torch.empty_like(inputs[0][0])
+    od = torch.empty_like(o)
+    lse_now = torch.empty(inputs[0][0].shape[:3], dtype=torch.float32, device="cuda")
+    dense_ms, own_masks = [], {}
+    for st, (q, k, v) in enumerate(inputs):  # the dense reference of every step
+        c, d_ = ev(), ev()
+        c.record()
+        cba.dense_attn_fwd(q, k, v, block=B, o=od)
+        d_.record()
+        torch.cuda.synchronize()
+        dense_ms.append(c.elapsed_time(d_))
+        if st in search_steps and st > 0:
+            e_own, _, _ = cba.calib_block_energy(q, k, None, **kw)
+            own_masks[st] = cba.select_blocks_by_energy_heads(e_own, taus, cfg.rho, True, cfg.n_prefix_blocks)
+            del e_own
+    out = {"search_steps": list(search_steps), "tau": cfg.tau, "dense_ms": dense_ms}
+    for source in ("cached", "sparse"):
+        lse = None
+        row_ptr = col_idx = None
+        steps = []
+        for st, (q, k, v) in enumerate(inputs):
+            a, b_ = ev(), ev()
+            search = st in search_steps
+            torch.cuda.synchronize()
+            a.record()
+            if st == 0:
+                energy, lse, _ = cba.calib_block_energy(q, k, v, o=o, **kw)
+            elif search and source == "sparse":
+                cba.sparse_attn_fwd(q, k, v, row_ptr, col_idx, o=o, lse=lse_now, **kw)
+                energy = cba.block_energy_from_lse(q, k, lse_now, **kw)
+            else:
+                cba.sparse_attn_fwd(q, k, v, row_ptr, col_idx, o=o, **kw)
+                if search:
+                    energy = cba.block_energy_from_lse(q, k, lse, **kw)
+            if search:
+                mask = cba.select_blocks_by_energy_heads(energy, taus, cfg.rho, True, cfg.n_prefix_blocks)
+                row_ptr, col_idx, _ = cba.build_block_csr(mask, with_order=False)
+            b_.record()
+            torch.cuda.synchronize()
+            cba.dense_attn_fwd(q, k, v, block=B, o=od)
+            rel = float((o.float() - od.float()).norm() / od.float().norm())
+            rec = {"step": st, "kind": "search" if search else "reuse", "ms": a.elapsed_time(b_),
+                   "rel_err_vs_dense": rel}
+            if search:
+                rec["density"] = float(mask.float().mean())
+                if st in own_masks:
+                    rec["mask_agreement_vs_own_lse"] = float((own_masks[st] == mask).float().mean())
+            steps.append(rec)
+            log(f"  [{source} LSE] step {st} {rec['kind']}: {rec['ms']:.1f} ms (dense {dense_ms[st]:.1f} ms), "
+                f"rel err {rel:.2e}" + (f", density {rec['density']:.3f}" if search else "")
+                + (f", mask agreement {rec['mask_agreement_vs_own_lse']:.4f}"
+                   if "mask_agreement_vs_own_lse" in rec else ""))
+        tot = sum(r["ms"] for r in steps)
+        out[source + "_lse"] = {"steps": steps, "total_ms": tot, "speedup_vs_dense": sum(dense_ms) / tot}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +388,9 @@ def main():
     ap.add_argument("--tau-schedule", default="",
                     help="comma-separated energy thresholds, one per timestep bucket of the calibrated workloads "
                          "(early buckets first); default: each workload's own tau")
+    ap.add_argument("--online-search", default="",
+                    help="a calibrated workload (e.g. hunyuan) to run the online search-and-reuse schedule on "
+                         "(8 steps, searches at steps 0 and 4)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -468,6 +556,9 @@ def main():
         torch.cuda.empty_cache()
         sched = [float(x) for x in args.tau_schedule.split(",")] if args.tau_schedule else None
         rows["calibrated"] = {name: calibrated_workload(name, tau_schedule=sched) for name in names}
+
+    if args.online_search:
+        rows["online_search"] = online_search(args.online_search)
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
