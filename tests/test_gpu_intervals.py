@@ -36,6 +36,8 @@ MASKS = [
     ("single column", lambda rng: (rng.random((50, 1)) < 0.5).astype(np.uint8)),
     ("runs across chunks", lambda rng: np.tile(np.r_[np.zeros(60), np.ones(70), np.zeros(3), np.ones(130)]
                                                .astype(np.uint8), (3, 1))),
+    ("wide rows", lambda rng: (rng.random((6, 65535)) < rng.uniform(0.001, 0.999, (6, 1))).astype(np.uint8)),
+    ("one long run", lambda rng: np.pad(np.ones((2, 65533), np.uint8), ((0, 0), (1, 1)))),
 ]
 
 

@@ -60,7 +60,7 @@ def test_energy_from_cached_lse(d, block, grid, n_prefix, dtype):
     log(f"  ok max |dE| {worst:.2e} of the query block's total weight")
 
 
-@pytest.mark.parametrize("draws,heads,nb,prefix", [(1, 4, 37, 0), (3, 40, 65, 2), (2, 256, 9, 1)])
+@pytest.mark.parametrize("draws,heads,nb,prefix", [(1, 4, 37, 0), (3, 40, 65, 2), (2, 256, 9, 1), (1, 2, 4096, 0)])
 def test_select_per_head_tau_bitexact(draws, heads, nb, prefix):
     rng = np.random.default_rng(draws * 100 + heads)
     energy = rng.gamma(0.6, 1.0, (draws, heads, nb, nb)).astype(np.float32)
