@@ -328,22 +328,25 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParam
 }
 
 // Block energy, sweep 2: E[qb, kb] = sum over the tile of exp(s_ij - lse_i), with
-// lse cached by the dense sweep.  One workgroup per (query block, batch item); each
-// wave sums its 32 rows' probabilities per key block in-lane, reduces across the
-// wave, and the per-wave partials are added in wave order at the end, so the
-// result is deterministic.
-template <int D, int B, bool BUF>
-__global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnParams p) {
+// lse cached by the dense sweep.  One workgroup per QPB consecutive query blocks of
+// one (head, batch item): every key tile staged in LDS serves QPB * B query rows.
+// Each wave sums its 32 rows' probabilities per key block in-lane, reduces across
+// the wave, and the per-wave partials of each query block are added in wave order
+// at the end, so the result is deterministic and independent of QPB.
+template <int D, int B, int QPB, bool BUF>
+__global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnParams p) {
   using C = Cfg<D, B>;
+  constexpr int WPB = C::NW, NW = QPB * WPB, NT = NW * 64;  // waves per query block, per workgroup
   __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
   extern __shared__ float part[];  // [NW][nb]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int item = blockIdx.x;
   const int it = item / p.batch, b = item - it * p.batch;
-  const int h = it / p.nb, qb = it - h * p.nb;
-  const int q0 = qb * B;
-  const int M = min(B, p.n - q0);
+  const int nqg = (p.nb + QPB - 1) / QPB;
+  const int h = it / nqg, qb0 = (it - h * nqg) * QPB;
+  const int q0 = qb0 * B;
+  const int M = min(QPB * B, p.n - q0);
 
   const int64_t head_off = (int64_t)b * p.sb + (int64_t)h * p.sh;
   const bfraw* qg = static_cast<const bfraw*>(p.q) + head_off;
@@ -367,14 +370,14 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnPar
     const int k0 = (s / C::SPB) * B + (s % C::SPB) * C::KT;
     return k0 < p.n ? k0 : -1;
   };
-  constexpr int LPW = C::KT / (64 / (D / 8)) / C::NW;
+  constexpr int LPW = C::KT / (64 / (D / 8)) / NW;
   int voff[LPW];
-  if (BUF) tile_lane_offsets<D, C::KT, C::NW>((int)(p.sn * 2), voff);
+  if (BUF) tile_lane_offsets<D, C::KT, NW>((int)(p.sn * 2), voff);
   const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto load = [&](int k0, bfraw* kdst) {
     if (BUF) load_tile_buf(kg, nrec, voff, LPW, k0 * (int)(p.sn * 2), kdst + wv * LPW * 512);
-    else load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0, kdst);
+    else load_tile<D, C::KT, NW>(kg, p.sn, p.n, k0, kdst);
   };
   float esum = 0.f;
   int k0_cur = step_key0(0);
@@ -428,11 +431,13 @@ __global__ __launch_bounds__((Cfg<D, B>::NT), 2) void energy_bf16_kernel(AttnPar
   }
   if (s < nsteps) step(s, k0s, k1s);
   __syncthreads();
-  float* eg = p.energy + (((int64_t)b * p.heads + h) * p.nb + qb) * p.nb;
-  for (int kb = tid; kb < p.nb; kb += C::NT) {
+  for (int idx = tid; idx < QPB * p.nb; idx += NT) {
+    const int j = idx / p.nb, kb = idx - j * p.nb;
+    const int qb = qb0 + j;
+    if (qb >= p.nb) continue;
     float e = 0.f;
-    for (int w = 0; w < C::NW; ++w) e += part[w * p.nb + kb];
-    eg[kb] = e;
+    for (int w = j * WPB; w < (j + 1) * WPB; ++w) e += part[w * p.nb + kb];
+    p.energy[(((int64_t)b * p.heads + h) * p.nb + qb) * p.nb + kb] = e;
   }
 }
 
@@ -462,18 +467,40 @@ hipError_t launch_attn_t(const AttnParams& p, bool with_pv, hipStream_t stream) 
   return hipLaunchKernel((const void*)kern, grid, block, args, lds, stream);
 }
 
+// Query blocks per energy workgroup: about 256 query rows (8 waves) share each K
+// tile, as far as the tile splits over the waves.
 template <int D, int B>
-hipError_t launch_energy_t(const AttnParams& p, hipStream_t stream) {
+constexpr int energy_qpb() {
   using C = Cfg<D, B>;
-  const size_t lds = (size_t)C::NW * p.nb * sizeof(float);
-  const dim3 grid((unsigned)((int64_t)p.heads * p.nb * p.batch)), block(C::NT);
+  constexpr int max_waves = C::KT * D / 512;  // one 1 KB tile load per wave at least
+  constexpr int waves = max_waves < 8 ? max_waves : 8;
+  return waves / C::NW > 0 ? waves / C::NW : 1;
+}
+
+template <int D, int B, int QPB>
+hipError_t launch_energy_q(const AttnParams& p, hipStream_t stream) {
+  using C = Cfg<D, B>;
+  const size_t lds = (size_t)QPB * C::NW * p.nb * sizeof(float);
+  const int64_t nqg = (p.nb + QPB - 1) / QPB;
+  const dim3 grid((unsigned)((int64_t)p.heads * nqg * p.batch)), block(QPB * C::NT);
   const bool buf = (int64_t)(p.n + C::KT) * p.sn * 2 < ((int64_t)1 << 31);
-  auto kern = buf ? energy_bf16_kernel<D, B, true> : energy_bf16_kernel<D, B, false>;
+  auto kern = buf ? energy_bf16_kernel<D, B, QPB, true> : energy_bf16_kernel<D, B, QPB, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   AttnParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel((const void*)kern, grid, block, args, lds, stream);
+}
+
+template <int D, int B>
+hipError_t launch_energy_t(const AttnParams& p, hipStream_t stream) {
+  using C = Cfg<D, B>;
+  constexpr int Q = energy_qpb<D, B>();
+  // The per-wave partials grow with the waves: fall back to one query block per
+  // workgroup when they would keep two workgroups from sharing a CU.
+  const size_t lds = (size_t)Q * C::NW * p.nb * sizeof(float) + 2 * C::TILE * 2;
+  if (Q > 1 && lds <= 64 * 1024) return launch_energy_q<D, B, Q>(p, stream);
+  return launch_energy_q<D, B, 1>(p, stream);
 }
 
 }  // namespace
