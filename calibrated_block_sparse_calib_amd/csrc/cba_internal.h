@@ -69,10 +69,12 @@ struct RepParams {
 // follower row) x (follower sub-groups of NWV - 1 rows) x (chunks of the frame x
 // column pairs), per batch item and head.  NWV = 2 waves for stride 2, else 4;
 // chunks are 32 pairs wide for bf16 and 64 for fp32.
+constexpr int kRepGroups = 2;  // bf16: column groups (of 32 pairs) per workgroup, sharing K tiles
+
 inline int64_t rep_grid(int batch, int heads, int gf, int gh, int gw, int stride, bool bf16, int* n_groups,
                         int* n_sub, int* n_chunks) {
   const int nf = stride == 2 ? 1 : 3;
-  const int cw = bf16 ? 32 : 64;
+  const int cw = bf16 ? 32 * kRepGroups : 64;
   *n_groups = (gh - 1 + stride - 1) / stride;
   *n_sub = (stride - 1 + nf - 1) / nf;
   *n_chunks = (int)(((int64_t)gf * gw + cw - 1) / cw);

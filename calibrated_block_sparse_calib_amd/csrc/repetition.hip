@@ -4,13 +4,14 @@
 // per-head mean, and the repetition flags from the means over calibration inputs.
 //
 // Work decomposition (bf16): one workgroup per (batch item and head, row group,
-// follower sub-group, chunk of 32 (frame, column) pairs).  Wave 0 computes the
-// anchor row of the group and waves 1..NWV-1 up to NWV-1 of its follower rows, all
-// for the same 32 (frame, column) pairs, so lane l of every wave holds the same
-// column and, in the MFMA accumulator layout, the same keys.  All waves walk the
-// whole key sequence together, sharing each K tile staged in LDS (double
-// buffered, one barrier per step).  Per step the anchor wave writes its 64 x 32
-// probabilities to an LDS exchange buffer; the follower waves keep their own
+// follower sub-group, chunk of 2 x 32 (frame, column) pairs).  For each 32-pair
+// column group, one wave computes the anchor row of the row group and NWV-1 waves
+// up to NWV-1 of its follower rows, all for the same 32 (frame, column) pairs, so
+// lane l of each of those waves holds the same column and, in the MFMA accumulator
+// layout, the same keys.  All waves of the workgroup walk the whole key sequence
+// together, sharing each K tile staged in LDS (double buffered, one barrier per
+// step) between both column groups.  Per step the anchor wave writes its 64 x 32
+// probabilities to its group's LDS exchange buffer; the follower waves keep their own
 // probabilities in registers and combine them with the anchor's one step later,
 // after the next barrier, so no extra barrier is needed.  Scores are computed
 // transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16.
@@ -29,13 +30,14 @@ using namespace dev;
 constexpr int kKT = 64;  // keys per step (bf16)
 
 template <int D, int NWV, bool BUF>
-__global__ __launch_bounds__(NWV * 64, 2) void rep_sim_bf16_kernel(RepParams p) {
-  constexpr int KS = D / 16, TILE = kKT * D;
+__global__ __launch_bounds__(kRepGroups * NWV * 64, 2) void rep_sim_bf16_kernel(RepParams p) {
+  constexpr int KS = D / 16, TILE = kKT * D, NW = kRepGroups * NWV;
   __shared__ __attribute__((aligned(16))) bfraw k0s[TILE], k1s[TILE];
-  __shared__ __attribute__((aligned(16))) float xch[2][8 * 64 * 4];  // [buffer][float4 j][lane]
-  __shared__ float anrm[32];
+  __shared__ __attribute__((aligned(16))) float xch[kRepGroups][2][8 * 64 * 4];  // [group][buffer][float4 j][lane]
+  __shared__ float anrm[kRepGroups][32];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+  const int wave = tid >> 6, gl = wave / NWV, wl = wave - gl * NWV;  // column group, wave in the group
   int item = blockIdx.x;
   const int chunk = item % p.n_chunks;
   item /= p.n_chunks;
@@ -47,10 +49,10 @@ __global__ __launch_bounds__(NWV * 64, 2) void rep_sim_bf16_kernel(RepParams p) 
 
   const int y0 = grp * p.stride;
   const int rows = min(p.stride, p.gh - y0);
-  const int r = wave == 0 ? 0 : 1 + sub * (NWV - 1) + (wave - 1);
+  const int r = wl == 0 ? 0 : 1 + sub * (NWV - 1) + (wl - 1);
   const bool active = r < rows;
   const int npairs = p.gf * p.gw;
-  const int u = chunk * 32 + (lane & 31);
+  const int u = (chunk * kRepGroups + gl) * 32 + (lane & 31);
   const bool u_valid = u < npairs;
   const int uu = u_valid ? u : npairs - 1;  // surplus lanes recompute the last column
   const int f = uu / p.gw, x = uu - f * p.gw;
@@ -67,21 +69,21 @@ __global__ __launch_bounds__(NWV * 64, 2) void rep_sim_bf16_kernel(RepParams p) 
   const float lse2 = p.lse[row_base + tok] * kLog2e;
 
   const int nsteps = (p.n + kKT - 1) / kKT;
-  constexpr int LPW = kKT / (64 / (D / 8)) / NWV;
+  constexpr int LPW = kKT / (64 / (D / 8)) / NW;
   int voff[LPW];
-  if (BUF) tile_lane_offsets<D, kKT, NWV>((int)(p.sn * 2), voff);
+  if (BUF) tile_lane_offsets<D, kKT, NW>((int)(p.sn * 2), voff);
   const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto load = [&](int k0, bfraw* kdst) __attribute__((always_inline)) {
     if (BUF) load_tile_buf(kg, nrec, voff, LPW, k0 * (int)(p.sn * 2), kdst + wv * LPW * 512);
-    else load_tile<D, kKT, NWV>(kg, p.sn, p.n, k0, kdst);
+    else load_tile<D, kKT, NW>(kg, p.sn, p.n, k0, kdst);
   };
 
   float pv[32];    // this step's probabilities (follower waves: last step's, until combined)
   float dot = 0.f, nrm = 0.f;
   auto combine = [&](int buf) __attribute__((always_inline)) {
     // pv holds this wave's probabilities of the step whose anchor values are in xch[buf].
-    const float4* src = reinterpret_cast<const float4*>(xch[buf]);
+    const float4* src = reinterpret_cast<const float4*>(xch[gl][buf]);
     float d_step = 0.f, n_step = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void rep_sim_bf16_kernel(RepParams p) 
     __syncthreads();
     // Follower waves first fold in the previous step: its anchor values became
     // visible at this barrier.
-    if (wave > 0 && active && s > 0) combine((s - 1) & 1);
+    if (wl > 0 && active && s > 0) combine((s - 1) & 1);
     if (s + 1 < nsteps) load((s + 1) * kKT, kn);
     if (!active) continue;
     const int k0 = s * kKT;
@@ -133,8 +135,8 @@ __global__ __launch_bounds__(NWV * 64, 2) void rep_sim_bf16_kernel(RepParams p) 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv[t * 16 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], p.c, -lse2));
-    if (wave == 0) {
-      float4* dst = reinterpret_cast<float4*>(xch[s & 1]);
+    if (wl == 0) {
+      float4* dst = reinterpret_cast<float4*>(xch[gl][s & 1]);
       float n_step = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -146,14 +148,14 @@ __global__ __launch_bounds__(NWV * 64, 2) void rep_sim_bf16_kernel(RepParams p) 
     }
   }
   __syncthreads();
-  if (wave > 0 && active) combine((nsteps - 1) & 1);
+  if (wl > 0 && active) combine((nsteps - 1) & 1);
   // Each lane holds half of its column's keys; add the other half's.
   dot += other_half(dot);
   nrm += other_half(nrm);
-  if (wave == 0 && lane < 32) anrm[lane] = nrm;
+  if (wl == 0 && lane < 32) anrm[gl][lane] = nrm;
   __syncthreads();
-  if (wave > 0 && active && u_valid && g == 0) {
-    p.token_cos[row_base + tok] = dot / sqrtf(nrm * anrm[lane]);
+  if (wl > 0 && active && u_valid && g == 0) {
+    p.token_cos[row_base + tok] = dot / sqrtf(nrm * anrm[gl][lane]);
   }
 }
 
@@ -286,7 +288,8 @@ hipError_t launch_sim_t(const RepParams& p, bool bf16, hipStream_t stream) {
     kern = rep_sim_f32_kernel<D, NWV>;
   }
   void* args[] = {&arg};
-  hipError_t e = hipLaunchKernel((const void*)kern, dim3((unsigned)items), dim3(NWV * 64), args, 0, stream);
+  hipError_t e = hipLaunchKernel((const void*)kern, dim3((unsigned)items), dim3((bf16 ? kRepGroups : 1) * NWV * 64),
+                                 args, 0, stream);
   if (e != hipSuccess) return e;
   return hipLaunchKernel((const void*)rep_mean_kernel, dim3((unsigned)(p.batch * p.heads)), dim3(kMeanThreads),
                          args, 0, stream);
