@@ -220,14 +220,15 @@ CBA_API cba_status sparse_attn_fwd_intervals(const cba_attn_desc* desc, const vo
   if (!iv_ptr || iv_len < 0 || (iv_len > 0 && !ivs)) return CBA_EINVAL;
   AttnParams p = make_params(desc);
   if ((st = set_rep(p, desc, rep_heads, anchor_stride))) return st;
-  static const uint32_t kNoRuns = 0;  // a non-null list for iv_len == 0 (never read)
   p.q = q;
   p.k = k;
   p.v = v;
   p.o = o;
   p.lse = lse;
   p.row_ptr = iv_ptr;
-  p.ivs = iv_len > 0 ? ivs : &kNoRuns;
+  // A non-null runs pointer selects interval mode; with iv_len == 0 no row has a run
+  // and the pointer is never read, so any device address serves.
+  p.ivs = iv_len > 0 ? ivs : reinterpret_cast<const uint32_t*>(iv_ptr);
   p.col_len = iv_len;
   p.work_order = work_order;
   p.fuse_broadcast = fuse_broadcast != 0;

@@ -158,3 +158,23 @@ def test_sparse_intervals_full_size_bitidentical(name):
     assert torch.equal(o_c, o_i) and torch.equal(l_c, l_i)
     rp, _, _, _ = oracle.build_intervals(mask.reshape(-1, cfg.nb))
     log(f"  {name}: {int(mask.sum())} kept blocks in {int(rp[-1])} runs; outputs bit-identical")
+
+
+def test_sparse_intervals_without_runs():
+    """iv_len = 0: no row has a run, so every output is 0 and every LSE -inf."""
+    import ctypes
+    cfg = _small_cfg(128, 128, (2, 8, 16), 0, heads=2)
+    q, k, v = make_qkv(cfg, draw=0)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o = torch.full_like(qd, 3.0)
+    lse = torch.zeros((1, cfg.heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+    iv_ptr = torch.zeros(cfg.heads * cfg.nb + 1, dtype=torch.int32, device="cuda")
+    desc = cba.make_desc(qd, cfg.block)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = cba.load_library().sparse_attn_fwd_intervals(ctypes.byref(desc), P(qd), P(kd), P(vd), P(iv_ptr), None, 0,
+                                                      None, None, 1, 0, P(o), P(lse),
+                                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.count_nonzero(o) == 0
+    assert torch.isneginf(lse).all()
