@@ -12,6 +12,7 @@ from .calibattn_oracle import (
     aggregate_votes,
     build_csr,
     build_intervals,
+    heavy_first_order,
     computed_rows,
     sparse_attention,
     row_broadcast,
@@ -31,6 +32,7 @@ __all__ = [
     "aggregate_votes",
     "build_csr",
     "build_intervals",
+    "heavy_first_order",
     "computed_rows",
     "sparse_attention",
     "row_broadcast",

@@ -44,7 +44,8 @@ below take as parameters):
      tokens; over calibration inputs the scores are averaged (fp64, input order)
      and the head is marked when the average is strictly above gamma;
   R22 a later search reuses the LSE cached by an earlier one as it is (no
-     correction): each row's energy terms are then scaled by one factor per row.
+     correction): each row's energy terms are then scaled by one factor per row;
+  R25 heavy rows (more kept blocks than a factor times the mean) run first.
 
 Parity pins: every function is pinned by tests against library routines, closed
 forms, invariants or brute force (tests/test_oracle.py).
@@ -217,6 +218,24 @@ def build_csr(mask):
     col_idx = np.nonzero(mask)[1].astype(np.int32)  # row-major scan: ascending per row
     work_order = np.argsort(-counts, kind="stable").astype(np.int32)
     return row_ptr, col_idx, work_order
+
+
+def heavy_first_order(counts, factor):
+    """Processing order of skip-list rows: the heavy rows first, the rest in place.
+
+    [AdaSpa] S2 balances the work of rows (heads) of differing density; here only
+    the rows much longer than the average are moved ahead, so that no long row
+    starts last, while the others keep the natural order that neighbouring rows
+    share keys in (R25).  heavy: kept count > factor * (mean kept count), compared
+    in fp64; heavy rows by (count descending, row ascending), then the other rows
+    ascending.  counts: [rows].  Returns int32 [rows].
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    thr = float(factor) * (float(counts.sum()) / float(counts.size))
+    heavy = np.nonzero(counts > thr)[0]
+    heavy = heavy[np.argsort(-counts[heavy], kind="stable")]
+    light = np.nonzero(counts <= thr)[0]
+    return np.concatenate([heavy, light]).astype(np.int32)
 
 
 def build_intervals(mask):

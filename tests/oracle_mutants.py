@@ -194,6 +194,16 @@ def select_first_head_tau(energy, tau, rho=0.5, force_diag=True, n_dense_prefix_
     return _orig["select_blocks"](energy, np.ravel(np.asarray(tau))[0], rho, force_diag, n_dense_prefix_blocks)
 
 
+def heavy_first_at_least(counts, factor):
+    """Rows equal to the threshold counted as heavy."""
+    counts = np.asarray(counts, dtype=np.int64)
+    thr = float(factor) * (float(counts.sum()) / float(counts.size))
+    heavy = np.nonzero(counts >= thr)[0]
+    heavy = heavy[np.argsort(-counts[heavy], kind="stable")]
+    light = np.nonzero(counts < thr)[0]
+    return np.concatenate([heavy, light]).astype(np.int32)
+
+
 MUTANTS = {
     "dense_no_scale": ("dense_attention", dense_no_scale),
     "dense_softmax_over_queries": ("dense_attention", dense_softmax_over_queries),
@@ -216,6 +226,7 @@ MUTANTS = {
     "intervals_inclusive_end": ("build_intervals", intervals_inclusive_end),
     "energy_from_lse_recomputed": ("block_energy_from_lse", energy_from_lse_recomputed),
     "select_first_head_tau": ("select_blocks", select_first_head_tau),
+    "heavy_first_at_least": ("heavy_first_order", heavy_first_at_least),
 }
 
 

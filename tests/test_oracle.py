@@ -564,3 +564,23 @@ def test_hand_per_head_tau_selection():
     b, vb = oracle.select_blocks(en, 0.8, 0.5)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(va, vb)
+
+
+def test_hand_heavy_first_order():
+    g = GOLD["heavy_first_example"]
+    for f in ("1.5", "1.6", "2", "3"):
+        np.testing.assert_array_equal(oracle.heavy_first_order(g["counts"], float(f)), g["order_" + f])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_heavy_first_order_limits(seed):
+    rng = np.random.default_rng(seed)
+    m = rng.random((60, 30)) < rng.uniform(0.05, 0.9, (60, 1))
+    counts = m.sum(axis=1)
+    for f in (0.5, 1.0, 1.7):
+        order = oracle.heavy_first_order(counts, f)
+        assert sorted(order.tolist()) == list(range(60))  # a permutation
+    # factor 0: every row with a kept block is heavy, so the order is longest-first
+    np.testing.assert_array_equal(oracle.heavy_first_order(counts, 0.0), oracle.build_csr(m)[2])
+    # a factor no row reaches leaves the natural order
+    np.testing.assert_array_equal(oracle.heavy_first_order(counts, 1e9), np.arange(60))
