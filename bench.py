@@ -201,9 +201,10 @@ def density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S
 
 def calibrated_workload(name, reps=2, tau_schedule=None):
     """One calibrated workload end to end: calib_block_energy over every draw
-    (LSE-only dense sweep + energy sweep), select_blocks_by_energy, build_block_csr
-    and sparse_attn_fwd on a held-out draw, the same through block intervals, plus
-    dense_attn_fwd for the speedup.  Per timestep bucket when the workload has
+    (LSE-only dense sweep + energy sweep), select_blocks_by_energy, build_block_csr,
+    the heavy-rows-first order, and sparse_attn_fwd on a held-out draw (also in
+    natural order, and through block intervals), plus dense_attn_fwd for the
+    speedup.  Per timestep bucket when the workload has
     several; tau_schedule gives each bucket its own energy threshold (early
     buckets first), else every bucket uses the workload's tau."""
     import torch
@@ -251,14 +252,19 @@ def calibrated_workload(name, reps=2, tau_schedule=None):
                                                         mask=mask))
         row_ptr, col_idx, _ = cba.build_block_csr(mask, with_order=False)
         c_ms = timed(lambda: cba.build_block_csr(mask, with_order=False))
+        # heavy rows (the dense text rows) first, the rest in natural order
+        order = cba.order_heavy_rows_first(row_ptr, cfg.nb, 2.0)
+        o_ms = timed(lambda: cba.order_heavy_rows_first(row_ptr, cfg.nb, 2.0, work_order=order))
         o = torch.empty_like(qd)
+        spn_ms = timed(lambda: cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, block=B, n_prefix=cfg.n_prefix,
+                                                   grid=cfg.grid, o=o))
         sp_ms = timed(lambda: cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, block=B, n_prefix=cfg.n_prefix,
-                                                  grid=cfg.grid, o=o))
+                                                  grid=cfg.grid, o=o, work_order=order))
         iv_ptr, ivs = cba.build_block_intervals(mask)
         ivb_ms = timed(lambda: cba.build_block_intervals(mask))
         o_iv = torch.empty_like(qd)
         iv_ms = timed(lambda: cba.sparse_attn_fwd_intervals(qd, kd, vd, iv_ptr, ivs, block=B, n_prefix=cfg.n_prefix,
-                                                            grid=cfg.grid, o=o_iv))
+                                                            grid=cfg.grid, o=o_iv, work_order=order))
         same = bool(torch.equal(o, o_iv))
         n_runs = int(iv_ptr[-1].item())
         del o_iv, iv_ptr, ivs
@@ -269,13 +275,14 @@ def calibrated_workload(name, reps=2, tau_schedule=None):
         res.update({"bucket": bucket, "tau": tau, "draws": cfg.calib_draws, "calib_ms": e_ms,
                     "calib_tflops": cal_flops / e_ms / 1e9, "select_ms": s_ms, "csr_ms": c_ms,
                     "mask_density": float(m.mean()), "head_density_min": float(dens.min()),
-                    "head_density_max": float(dens.max()), "sparse_ms": sp_ms, "sparse_tflops": kept / sp_ms / 1e9,
+                    "head_density_max": float(dens.max()), "order_ms": o_ms, "sparse_natural_order_ms": spn_ms,
+                    "sparse_ms": sp_ms, "sparse_tflops": kept / sp_ms / 1e9,
                     "dense_ms": de_ms, "speedup_vs_dense": de_ms / sp_ms,
                     "intervals_build_ms": ivb_ms, "sparse_intervals_ms": iv_ms, "intervals_same_output": same,
                     "runs": n_runs, "kept_blocks": int(m.sum()),
                     "skip_list_bytes": skip_list_bytes(H * cfg.nb, cfg.nb, int(m.sum()), n_runs)})
         log(f"{name} bucket {bucket}: calibration {e_ms:.1f} ms ({res['calib_tflops']:.0f} TFLOP/s), select "
-            f"{s_ms:.2f} ms, density {res['mask_density']:.3f}, sparse {sp_ms:.2f} ms "
+            f"{s_ms:.2f} ms, density {res['mask_density']:.3f}, sparse {sp_ms:.2f} ms (natural order {spn_ms:.2f}) "
             f"({res['sparse_tflops']:.0f} TFLOP/s kept), dense {de_ms:.2f} ms; intervals: {n_runs} runs for "
             f"{int(m.sum())} blocks, sparse {iv_ms:.2f} ms")
         out.append(res)

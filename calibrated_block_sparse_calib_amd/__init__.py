@@ -12,6 +12,7 @@ from .api import (
     dense_attn_fwd,
     make_desc,
     n_blocks,
+    order_heavy_rows_first,
     rep_row_broadcast,
     select_blocks_by_energy,
     select_blocks_by_energy_heads,
@@ -35,6 +36,7 @@ __all__ = [
     "load_library",
     "make_desc",
     "n_blocks",
+    "order_heavy_rows_first",
     "rep_row_broadcast",
     "select_blocks_by_energy",
     "select_blocks_by_energy_heads",

@@ -193,6 +193,23 @@ def build_block_csr(mask: torch.Tensor, with_order: bool = True, exact: bool = F
     return row_ptr, col_idx, order
 
 
+def order_heavy_rows_first(row_ptr: torch.Tensor, nkb: int, factor: float = 2.0,
+                           work_order: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row order with the rows holding more than factor x the mean kept blocks first
+    (longest first), then the other rows in place.  row_ptr from build_block_csr."""
+    _require_gpu(row_ptr, work_order)
+    if row_ptr.dtype != torch.int32 or not row_ptr.is_contiguous():
+        raise CalibAttnError("row_ptr must be contiguous int32")
+    rows = row_ptr.numel() - 1
+    if work_order is None:
+        work_order = torch.empty(rows, dtype=torch.int32, device=row_ptr.device)
+    if work_order.dtype != torch.int32 or work_order.numel() != rows:
+        raise CalibAttnError("work_order must be int32 [rows]")
+    _check(_lib.load().order_heavy_rows_first(_ptr(row_ptr), rows, int(nkb), float(factor), _ptr(work_order),
+                                              _stream()), "order_heavy_rows_first")
+    return work_order
+
+
 def build_block_intervals(mask: torch.Tensor, exact: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """mask uint8 [..., nkb] (rows = all leading dims) -> (iv_ptr int32 [rows + 1],
     ivs [capacity]): the maximal runs of kept blocks of every row, each packed as

@@ -200,6 +200,14 @@ CBA_API cba_status sparse_attn_fwd(const cba_attn_desc* desc, const void* q, con
   return from_hip(run_attention(p, desc, /*with_pv=*/true, reinterpret_cast<hipStream_t>(stream)));
 }
 
+CBA_API cba_status order_heavy_rows_first(const int32_t* row_ptr, int32_t n_rows, int32_t nkb, double factor,
+                                          int32_t* work_order, cba_stream_t stream) {
+  if (!row_ptr || !work_order || n_rows < 1 || nkb < 1) return CBA_EINVAL;
+  if ((int64_t)n_rows * nkb > INT32_MAX || !std::isfinite(factor) || factor < 0.0) return CBA_EINVAL;
+  return from_hip(cba::launch_heavy_order(row_ptr, n_rows, nkb, factor, work_order,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
 CBA_API cba_status build_block_intervals(const uint8_t* mask, int32_t n_rows, int32_t nkb, int32_t* iv_ptr,
                                          uint32_t* ivs, int64_t iv_capacity, cba_stream_t stream) {
   if (!mask || !iv_ptr || n_rows < 1 || nkb < 1 || nkb > 65535) return CBA_EINVAL;

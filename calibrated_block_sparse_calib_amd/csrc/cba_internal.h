@@ -93,6 +93,8 @@ hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, co
                          hipStream_t stream);
 hipError_t launch_csr(const uint8_t* mask, int n_rows, int nkb, int32_t* row_ptr, int32_t* col_idx,
                       int64_t capacity, int32_t* work_order, hipStream_t stream);
+hipError_t launch_heavy_order(const int32_t* row_ptr, int n_rows, int nkb, double factor, int32_t* work_order,
+                              hipStream_t stream);
 hipError_t launch_intervals(const uint8_t* mask, int n_rows, int nkb, int32_t* iv_ptr, uint32_t* ivs,
                             int64_t capacity, hipStream_t stream);
 hipError_t launch_broadcast(const AttnParams& p, int head_dim, int elem_bytes, hipStream_t stream);

@@ -202,15 +202,27 @@ __global__ __launch_bounds__(64 * kWaves) void csr_fill_kernel(const uint8_t* ma
 
 constexpr int kOrderThreads = 256;
 
+// Longest-first order (heavy_first = 0): workgroup c places the rows with kept
+// count c, in row order, after all rows with a larger count.  Heavy-first order
+// (heavy_first = 1): only counts above thr = factor * mean are placed that way;
+// one more workgroup (c = gridDim.x - 1) places every other row, in row order,
+// after all the heavy rows.
 __global__ __launch_bounds__(kOrderThreads) void csr_order_kernel(int n_rows, const int32_t* row_ptr,
-                                                                  int32_t* work_order) {
+                                                                  int32_t* work_order, int heavy_first,
+                                                                  double factor) {
   __shared__ int wcnt[kOrderThreads / 64];
   __shared__ int total_s;
   const int c = blockIdx.x;  // the kept count handled by this workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Rows with a larger count come first.
+  const double thr = heavy_first ? factor * ((double)row_ptr[n_rows] / (double)n_rows) : -1.0;
+  const bool light_group = heavy_first && c == (int)gridDim.x - 1;
+  if (heavy_first && !light_group && (double)c <= thr) return;  // light count: placed by the last group
+  // Rows placed before this group's: a larger count, or (light group) every heavy row.
   int gt = 0;
-  for (int r = tid; r < n_rows; r += kOrderThreads) gt += (row_ptr[r + 1] - row_ptr[r]) > c;
+  for (int r = tid; r < n_rows; r += kOrderThreads) {
+    const int cnt = row_ptr[r + 1] - row_ptr[r];
+    gt += light_group ? ((double)cnt > thr) : (cnt > c);
+  }
   for (int off = 32; off >= 1; off >>= 1) gt += __shfl_xor(gt, off, 64);
   if (lane == 0) wcnt[wave] = gt;
   __syncthreads();
@@ -224,7 +236,8 @@ __global__ __launch_bounds__(kOrderThreads) void csr_order_kernel(int n_rows, co
   __syncthreads();
   for (int base = 0; base < n_rows; base += kOrderThreads) {
     const int r = base + tid;
-    const bool f = r < n_rows && (row_ptr[r + 1] - row_ptr[r]) == c;
+    const int cnt = r < n_rows ? row_ptr[r + 1] - row_ptr[r] : 0;
+    const bool f = r < n_rows && (light_group ? (double)cnt <= thr : cnt == c);
     const uint64_t bal = __ballot(f);
     if (lane == 0) wcnt[wave] = __popcll(bal);
     __syncthreads();
@@ -358,10 +371,17 @@ hipError_t launch_csr(const uint8_t* mask, int n_rows, int nkb, int32_t* row_ptr
   }
   if (work_order) {
     hipLaunchKernelGGL(csr_order_kernel, dim3((unsigned)(nkb + 1)), dim3(kOrderThreads), 0, stream, n_rows,
-                       (const int32_t*)row_ptr, work_order);
+                       (const int32_t*)row_ptr, work_order, 0, 0.0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_heavy_order(const int32_t* row_ptr, int n_rows, int nkb, double factor, int32_t* work_order,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(csr_order_kernel, dim3((unsigned)(nkb + 2)), dim3(kOrderThreads), 0, stream, n_rows, row_ptr,
+                     work_order, 1, factor);
+  return hipGetLastError();
 }
 
 hipError_t launch_intervals(const uint8_t* mask, int n_rows, int nkb, int32_t* iv_ptr, uint32_t* ivs,

@@ -142,6 +142,22 @@ cba_status build_block_csr(const uint8_t* mask, int32_t n_rows, int32_t nkb, int
                            int32_t* col_idx, int64_t col_idx_capacity, int32_t* work_order,
                            cba_stream_t stream);
 
+/* Processing order of skip-list rows with only the heavy rows moved ahead (AdaSpa
+ * S2 balances the work of rows of differing density).  A row is heavy when its
+ * kept count row_ptr[r+1] - row_ptr[r] is above factor * (row_ptr[n_rows] /
+ * n_rows), computed in fp64.  work_order lists the heavy rows by (count
+ * descending, row ascending), then every other row in ascending order: long rows
+ * (such as the dense rows of text tokens) no longer start last, while the others
+ * keep the natural order in which neighbouring rows share key blocks.  factor = 0
+ * gives build_block_csr's longest-first order; a factor no row reaches gives the
+ * natural order.
+ *   row_ptr: int32 [n_rows + 1] from build_block_csr for a mask of nkb columns
+ *            (every count in [0, nkb]).
+ *   work_order: int32 [n_rows] output, a permutation of the rows.
+ * factor finite and >= 0.  Integer results, bit-exact. */
+cba_status order_heavy_rows_first(const int32_t* row_ptr, int32_t n_rows, int32_t nkb, double factor,
+                                  int32_t* work_order, cba_stream_t stream);
+
 /* Skip list as block intervals (zh S2.2B: the mask becomes a skip list holding
  * only the block intervals to compute): the maximal runs of consecutive kept
  * blocks of each mask row.  A compact form of the skip list for the per

@@ -31,7 +31,7 @@ def test_header_declares_every_call():
     for n in ["calib_block_energy", "select_blocks_by_energy", "build_block_csr", "sparse_attn_fwd",
               "rep_row_broadcast", "dense_attn_fwd", "spatial_rep_similarity", "select_rep_heads",
               "build_block_intervals", "sparse_attn_fwd_intervals", "block_energy_from_lse",
-              "select_blocks_by_energy_heads",
+              "select_blocks_by_energy_heads", "order_heavy_rows_first",
               "cba_status_str", "cba_version"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -190,3 +190,12 @@ def test_online_search_calls_reject_bad_arguments(lib):
     assert f(FAKE, 1, 300, 8, taus, 0.5, 1, 0, FAKE, None, None) == EINVAL  # beyond 256 heads
     assert f(FAKE, 1, 2, 5000, taus, 0.5, 1, 0, FAKE, None, None) == EINVAL
     assert f(None, 1, 2, 8, taus, 0.5, 1, 0, FAKE, None, None) == EINVAL
+
+
+def test_heavy_order_rejects_bad_arguments(lib):
+    f = lib.order_heavy_rows_first
+    assert f(None, 4, 4, 2.0, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 4, 2.0, None, None) == EINVAL
+    assert f(FAKE, 0, 4, 2.0, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 4, -1.0, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 4, float("inf"), FAKE, None) == EINVAL

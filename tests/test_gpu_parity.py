@@ -311,3 +311,23 @@ def test_wide_row_stride_takes_global_load_path():
     assert_close_out(to_host(o_w)[0], ref_o, "bf16", "wide-stride sparse O")
     del qw, kw, vw, ow, o_wi
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("factor", [0.0, 1.6, 2.0, 1e9])
+def test_heavy_first_order_bitexact(factor):
+    """order_heavy_rows_first against the oracle: the hand-derived counts, and a mask
+    with two dense rows per head (like text tokens) over random sparse rows."""
+    g_counts = np.array([3, 9, 2, 3, 12, 3, 0, 8])
+    hand = (np.arange(12)[None, :] < g_counts[:, None]).astype(np.uint8)
+    rng = np.random.default_rng(17)
+    m = (rng.random((6 * 50, 50)) < 0.15).astype(np.uint8)
+    m[::50] = 1
+    m[1::50] = 1
+    for mask in (hand, m):
+        row_ptr, _, lpt = cba.build_block_csr(torch.from_numpy(mask).cuda())
+        got = cba.order_heavy_rows_first(row_ptr, mask.shape[1], factor)
+        torch.cuda.synchronize()
+        ref = oracle.heavy_first_order(mask.sum(axis=1), factor)
+        np.testing.assert_array_equal(got.cpu().numpy(), ref)
+        if factor == 0.0:
+            assert torch.equal(got, lpt)
