@@ -67,16 +67,25 @@ def rows_per_block(cfg, is_rep):
     return np.concatenate([r, np.zeros(pad, bool)]).reshape(cfg.nb, cfg.block).sum(1).astype(np.int64)
 
 
-KERNEL_UNIT = ("attn_bf16.hip", "mfma_util.h", "cba_internal.h")  # the sparse kernel's translation unit
+KERNEL_UNIT = ("attn_bf16.hip", "mfma_util.h")  # the sparse kernel's own sources
 
 
 def source_hash():
-    """Hash of the sources compiled into the sparse kernel: byte counters taken on
-    another version of them are not reported."""
+    """Hash of the sources compiled into the sparse kernel (its file, the device
+    helpers, and the parameter block it reads from the shared header): byte
+    counters taken on another version of them are not reported."""
+    import re
+
     h = hashlib.sha256()
+    csrc = os.path.dirname(KERNEL_SOURCE)
     for name in KERNEL_UNIT:
-        with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
+    with open(os.path.join(csrc, "cba_internal.h")) as f:
+        hdr = f.read()
+    for pat in (r"struct AttnParams \{.*?\n\};", r"inline bool rep_head\(.*?\n\}", r"constexpr int kMaxRepHeads = \d+;"):
+        m = re.search(pat, hdr, re.S)
+        h.update(m.group(0).encode() if m else b"?")
     return h.hexdigest()[:16]
 
 
