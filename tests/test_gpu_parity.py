@@ -331,3 +331,59 @@ def test_heavy_first_order_bitexact(factor):
         np.testing.assert_array_equal(got.cpu().numpy(), ref)
         if factor == 0.0:
             assert torch.equal(got, lpt)
+
+
+def test_graph_capture_replays_match_eager():
+    """The calls allocate nothing and take the caller's stream, so a HIP graph can
+    capture them: skip-list build, sparse attention with a repetition head and the
+    separate broadcast, replayed several times with eager work in between; every
+    replay equals the eager result."""
+    cfg = _small_cfg(128, 64, (2, 8, 16), 0, heads=2)
+    q, k, v = make_qkv(cfg, draw=0)
+    mask = random_block_mask(cfg)
+    rep = rep_head_flags(cfg)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    md = torch.from_numpy(mask).cuda()
+    nb = cfg.nb
+    row_ptr = torch.empty(cfg.heads * nb + 1, dtype=torch.int32, device="cuda")
+    col_idx = torch.empty(cfg.heads * nb * nb, dtype=torch.int32, device="cuda")
+    order = torch.empty(cfg.heads * nb, dtype=torch.int32, device="cuda")
+    o = torch.zeros_like(qd)
+    import ctypes
+    lib = cba.load_library()
+    desc = cba.make_desc(qd, cfg.block, 0, cfg.grid)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    rep_arr = np.ascontiguousarray(rep)
+
+    def work():
+        S = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert lib.build_block_csr(P(md), cfg.heads * nb, nb, P(row_ptr), P(col_idx), col_idx.numel(), P(order),
+                                   S) == 0
+        assert lib.sparse_attn_fwd(ctypes.byref(desc), P(qd), P(kd), P(vd), P(row_ptr), P(col_idx), col_idx.numel(),
+                                   P(order), rep_arr.ctypes.data_as(ctypes.c_void_p), cfg.anchor_stride, 0, P(o),
+                                   None, S) == 0
+        assert lib.rep_row_broadcast(ctypes.byref(desc), P(o), rep_arr.ctypes.data_as(ctypes.c_void_p),
+                                     cfg.anchor_stride, S) == 0
+
+    work()
+    torch.cuda.synchronize()
+    eager = o.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep_i in range(4):
+        o.zero_()
+        row_ptr.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager), f"replay {rep_i} differs"
+        work()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager)
