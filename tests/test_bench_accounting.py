@@ -1,0 +1,64 @@
+"""The benchmark's work accounting on the CPU: kept-block FLOPs, computed rows per
+query block, rows of the repetition-similarity kernel and skip-list storage,
+each against a direct count over the token mask; and the one-GPU guard."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import oracle
+from workloads import AttnConfig, get_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _cfg():
+    return AttnConfig(name="acct", heads=3, head_dim=64, grid=(2, 7, 9), block=32, dtype="bf16", seed=1,
+                      n_prefix=32, anchor_stride=3)
+
+
+def test_kept_flops_counts_kept_key_tokens_of_computed_rows():
+    cfg = _cfg()
+    rng = np.random.default_rng(0)
+    mask = (rng.random((cfg.heads, cfg.nb, cfg.nb)) < 0.4).astype(np.uint8)
+    rep = np.array([0, 1, 0], np.uint8)
+    comp = (bench.rows_per_block(cfg, False), bench.rows_per_block(cfg, True))
+    got = bench.kept_flops(mask, cfg, rep, comp)
+    want = 0
+    for h in range(cfg.heads):
+        tok = oracle.token_mask_from_blocks(mask[h], cfg.block, cfg.seq_len)  # [N, N] kept pairs
+        rows = oracle.computed_rows(cfg.seq_len, cfg.n_prefix, cfg.grid, cfg.anchor_stride, bool(rep[h]))
+        want += int(tok[rows].sum())
+    assert got == 4 * cfg.head_dim * want
+
+
+def test_rows_per_block_match_computed_rows():
+    cfg = _cfg()
+    for is_rep in (False, True):
+        rows = oracle.computed_rows(cfg.seq_len, cfg.n_prefix, cfg.grid, cfg.anchor_stride, is_rep)
+        per_block = [int(rows[qb * cfg.block:(qb + 1) * cfg.block].sum()) for qb in range(cfg.nb)]
+        np.testing.assert_array_equal(bench.rows_per_block(cfg, is_rep), per_block)
+
+
+def test_rep_rows_per_head_counts_groups_with_followers():
+    for grid, s in (((21, 45, 80), 4), ((2, 6, 5), 3), ((1, 2, 7), 2), ((3, 9, 4), 4)):
+        cfg = AttnConfig(name="r", heads=1, head_dim=64, grid=grid, block=32, dtype="bf16", seed=0, anchor_stride=s)
+        f_, h_, w_ = grid
+        # every row of a group whose anchor row has at least one follower row below it
+        rows = sum(min(s, h_ - y0) for y0 in range(0, h_, s) if y0 + 1 < h_)
+        assert bench.rep_rows_per_head(cfg) == f_ * w_ * rows
+    assert bench.rep_rows_per_head(get_config("wan14_720p")) == 21 * 80 * 44
+
+
+def test_skip_list_bytes():
+    b = bench.skip_list_bytes(rows=10, nkb=20, nnz=37, runs=12)
+    assert b == {"bitmask": 10 * 3, "csr": 4 * (11 + 37), "intervals": 4 * (11 + 12)}
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
