@@ -9,7 +9,9 @@ from .api import (
     build_block_csr,
     build_block_intervals,
     calib_block_energy,
+    calib_block_energy_ws,
     dense_attn_fwd,
+    energy_workspace_bytes,
     make_desc,
     n_blocks,
     order_heavy_rows_first,
@@ -32,7 +34,9 @@ __all__ = [
     "build_block_csr",
     "build_block_intervals",
     "calib_block_energy",
+    "calib_block_energy_ws",
     "dense_attn_fwd",
+    "energy_workspace_bytes",
     "load_library",
     "make_desc",
     "n_blocks",

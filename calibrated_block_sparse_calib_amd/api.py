@@ -121,6 +121,39 @@ def select_blocks_by_energy(energy: torch.Tensor, tau: float, rho: float = 0.5, 
     return (mask, votes) if return_votes else mask
 
 
+def energy_workspace_bytes(q: torch.Tensor, block: int) -> int:
+    """Workspace size calib_block_energy_ws needs for q's shape."""
+    b, h, n, _ = q.shape
+    nb = n_blocks(n, block)
+    return b * h * nb * nb * block * 4
+
+
+def calib_block_energy_ws(q, k, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,
+                          workspace: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          energy: Optional[torch.Tensor] = None):
+    """Energies and LSE in one pass over the keys (no V), using a workspace of
+    energy_workspace_bytes(q, block) bytes (allocated here when not given).
+    Returns (energy, lse)."""
+    _require_gpu(q, k, workspace, lse, energy)
+    _same_layout(q, k)
+    desc = make_desc(q, block, n_prefix, grid, scale)
+    b, h, n, _ = q.shape
+    nb = n_blocks(n, block)
+    if lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if energy is None:
+        energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
+    need = energy_workspace_bytes(q, block)
+    if workspace is None:
+        workspace = torch.empty(need if q.dtype == torch.bfloat16 else 16, dtype=torch.uint8, device=q.device)
+    if not (lse.is_contiguous() and energy.is_contiguous() and workspace.is_contiguous()):
+        raise CalibAttnError("lse, energy and workspace must be contiguous")
+    _check(_lib.load().calib_block_energy_ws(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(energy),
+                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                             _stream()), "calib_block_energy_ws")
+    return energy, lse
+
+
 def block_energy_from_lse(q, k, lse, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,
                           energy: Optional[torch.Tensor] = None):
     """Energy sweep alone from a given (possibly cached) LSE fp32 [batch, heads, seq_len].

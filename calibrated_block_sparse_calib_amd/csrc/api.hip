@@ -119,6 +119,31 @@ CBA_API cba_status calib_block_energy(const cba_attn_desc* desc, const void* q, 
   return from_hip(e);
 }
 
+CBA_API cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* q, const void* k, float* lse,
+                                         float* energy, void* workspace, int64_t workspace_bytes,
+                                         cba_stream_t stream) {
+  cba_status st = check_desc(desc);
+  if (st) return st;
+  if (check_tensor(q) || check_tensor(k) || !lse || !energy) return CBA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(energy) & 3u)) return CBA_EINVAL;
+  AttnParams p = make_params(desc);
+  p.q = q;
+  p.k = k;
+  p.lse = lse;
+  p.energy = energy;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (desc->dtype != CBA_DTYPE_BF16) {
+    // fp32: the two sweeps (no workspace needed).
+    hipError_t e = run_attention(p, desc, /*with_pv=*/false, s);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(cba::launch_energy_f32(p, desc->head_dim, desc->block, s));
+  }
+  const int64_t need = (int64_t)desc->batch * desc->heads * p.nb * p.nb * desc->block * (int64_t)sizeof(float);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return CBA_EINVAL;
+  if (workspace_bytes < need) return CBA_ECAPACITY;
+  return from_hip(cba::launch_energy1_bf16(p, desc->head_dim, desc->block, static_cast<float*>(workspace), s));
+}
+
 CBA_API cba_status select_blocks_by_energy(const float* energy, int32_t n_draws, int32_t heads, int32_t nb,
                                            double tau, double rho, int32_t force_diag,
                                            int32_t n_dense_prefix_blocks, uint8_t* mask, int32_t* votes,

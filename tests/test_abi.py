@@ -31,7 +31,7 @@ def test_header_declares_every_call():
     for n in ["calib_block_energy", "select_blocks_by_energy", "build_block_csr", "sparse_attn_fwd",
               "rep_row_broadcast", "dense_attn_fwd", "spatial_rep_similarity", "select_rep_heads",
               "build_block_intervals", "sparse_attn_fwd_intervals", "block_energy_from_lse",
-              "select_blocks_by_energy_heads", "order_heavy_rows_first",
+              "select_blocks_by_energy_heads", "order_heavy_rows_first", "calib_block_energy_ws",
               "cba_status_str", "cba_version"]:
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -199,3 +199,14 @@ def test_heavy_order_rejects_bad_arguments(lib):
     assert f(FAKE, 0, 4, 2.0, FAKE, None) == EINVAL
     assert f(FAKE, 4, 4, -1.0, FAKE, None) == EINVAL
     assert f(FAKE, 4, 4, float("inf"), FAKE, None) == EINVAL
+
+
+def test_energy_ws_rejects_bad_arguments(lib):
+    d = _desc()  # bf16, 2 heads, 256 tokens, block 128: nb = 2, workspace 2*2*2*128*4 = 4096 bytes
+    assert lib.calib_block_energy_ws(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 4096, None) == EINVAL
+    assert lib.calib_block_energy_ws(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4095, None) == 4  # ECAPACITY
+    assert lib.calib_block_energy_ws(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, 4096, None) == EINVAL
+    assert lib.calib_block_energy_ws(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10004), 4096,
+                                     None) == EINVAL
+    assert lib.calib_block_energy_ws(ctypes.byref(_desc(block=48)), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                     None) == EUNSUPPORTED

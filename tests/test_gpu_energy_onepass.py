@@ -1,0 +1,90 @@
+"""GPU parity of the one-pass energy sweep (calib_block_energy_ws) against the fp64
+oracle: energies |dE| <= 1e-4 * block (bf16), LSE within 1e-3, repeated calls
+bit-identical, and the workspace size enforced."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import calibrated_block_sparse_calib_amd as cba
+import oracle
+from workloads import AttnConfig, get_config, make_qkv
+from tests.gpu_util import assert_close_lse, log, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(d, block, grid, n_prefix, heads=3):
+    return AttnConfig(name="e1", heads=heads, head_dim=d, grid=grid, block=block, dtype="bf16", seed=41,
+                      n_prefix=n_prefix, lt=2.0, ls=5.0)
+
+
+@pytest.mark.parametrize("d,block,grid,n_prefix", [
+    (128, 128, (2, 17, 20), 0),   # ragged last block of 40
+    (64, 64, (3, 9, 10), 64),
+    (128, 32, (2, 6, 11), 32),
+    (64, 128, (1, 13, 12), 128),
+    (128, 64, (2, 8, 8), 0),      # exact multiple
+    (128, 128, (1, 1, 5), 0),     # one short block
+])
+def test_onepass_energy_matches_oracle(d, block, grid, n_prefix):
+    cfg = _cfg(d, block, grid, n_prefix)
+    log(f"one-pass energy d={d} B={block} grid={grid} prefix={n_prefix}")
+    draws = [make_qkv(cfg, draw=i, with_v=False) for i in range(2)]
+    q = np.stack([x[0] for x in draws])
+    k = np.stack([x[1] for x in draws])
+    qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    kd = torch.from_numpy(k).to(torch.bfloat16).cuda()
+    e1, l1 = cba.calib_block_energy_ws(qd, kd, block=block)
+    e1b, l1b = cba.calib_block_energy_ws(qd, kd, block=block)
+    e2, l2, _ = cba.calib_block_energy(qd, kd, None, block=block)
+    torch.cuda.synchronize()
+    assert torch.equal(e1, e1b) and torch.equal(l1, l1b)
+    got_e, got_l = to_host(e1), to_host(l1)
+    worst = 0.0
+    for dr in range(2):
+        for h in range(cfg.heads):
+            ref = oracle.block_energy(q[dr, h], k[dr, h], block)
+            worst = max(worst, float(np.abs(got_e[dr, h] - ref).max()))
+            _, ref_lse = oracle.dense_attention(q[dr, h], k[dr, h], k[dr, h])
+            assert_close_lse(got_l[dr, h], ref_lse, f"one-pass LSE draw {dr} head {h}", 1e-3)
+    assert worst <= 1e-4 * block, f"energy error {worst:.3e}"
+    # against the two-sweep energies of the same inputs
+    assert float((e1 - e2).abs().max()) <= 2e-4 * block
+    log(f"  ok max |dE| {worst:.2e}")
+
+
+def test_onepass_workspace_too_small_is_refused():
+    cfg = _cfg(128, 128, (2, 8, 16), 0)
+    q, k, _ = make_qkv(cfg, draw=0, with_v=False)
+    qd = torch.from_numpy(q[None]).to(torch.bfloat16).cuda()
+    kd = torch.from_numpy(k[None]).to(torch.bfloat16).cuda()
+    need = cba.energy_workspace_bytes(qd, 128)
+    ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(cba.CalibAttnError):
+        cba.calib_block_energy_ws(qd, kd, block=128, workspace=ws)
+
+
+@pytest.mark.timeout(600)
+def test_onepass_energy_full_size_hunyuan():
+    """HunyuanVideo shape, one draw: sampled query blocks against the oracle and the
+    whole energy tensor against the two-sweep result."""
+    cfg = get_config("hunyuan")
+    q, k, _ = make_qkv(cfg, draw=0, with_v=False)
+    qd = torch.from_numpy(q[None]).to(torch.bfloat16).cuda()
+    kd = torch.from_numpy(k[None]).to(torch.bfloat16).cuda()
+    e1, l1 = cba.calib_block_energy_ws(qd, kd, block=cfg.block)
+    e2, l2, _ = cba.calib_block_energy(qd, kd, None, block=cfg.block)
+    torch.cuda.synchronize()
+    assert float((e1 - e2).abs().max()) <= 2e-4 * cfg.block
+    assert float((l1 - l2).abs().max()) <= 1e-3
+    got = to_host(e1)[0]
+    rng = np.random.default_rng(4)
+    worst = 0.0
+    for h, qb in [(0, 0), (cfg.heads - 1, cfg.nb - 1)] + [(int(a), int(b)) for a, b in
+                                                          zip(rng.integers(0, cfg.heads, 4), rng.integers(0, cfg.nb, 4))]:
+        ref = oracle.block_energy(q[h], k[h], cfg.block, q_blocks=[qb])[0]
+        worst = max(worst, float(np.abs(got[h, qb] - ref).max()))
+    log(f"  hunyuan one-pass: max |dE| {worst:.2e} on sampled rows")
+    assert worst <= 1e-4 * cfg.block
