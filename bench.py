@@ -11,7 +11,7 @@ resident in HBM before the timed region.
 A step is the inference path: build_block_csr (mask -> skip list and work order)
 then sparse_attn_fwd (kept blocks only, anchor rows of repetition heads, fused
 broadcast).  value = kept-block FLOPs / step time.  The other entry points
-(calib_block_energy, select_blocks_by_energy, spatial_rep_similarity,
+(calib_block_energy, calib_block_energy_ws, select_blocks_by_energy, spatial_rep_similarity,
 select_rep_heads, rep_row_broadcast, dense_attn_fwd) are timed in the same run and
 reported under "rows"; dense_attn_fwd gives the speedup.  The fp64 CPU oracle is timed on a bounded sample of query blocks of the
 same workload (cpu_baseline) and its outputs are compared with the GPU's.
@@ -209,8 +209,9 @@ def density_sweep(cfg, lib, desc, qd, kd, vd, od, row_ptr, col_idx, timeit, P, S
 
 
 def calibrated_workload(name, reps=2, tau_schedule=None):
-    """One calibrated workload end to end: calib_block_energy over every draw
-    (LSE-only dense sweep + energy sweep), select_blocks_by_energy, build_block_csr,
+    """One calibrated workload end to end: calib_block_energy_ws over every draw
+    (energies and LSE in one sweep; the two-sweep calib_block_energy is timed beside
+    it), select_blocks_by_energy, build_block_csr,
     the heavy-rows-first order, and sparse_attn_fwd on a held-out draw (also in
     natural order, and through block intervals), plus dense_attn_fwd for the
     speedup.  Per timestep bucket when the workload has
@@ -251,10 +252,17 @@ def calibrated_workload(name, reps=2, tau_schedule=None):
         del q, k, v
         log(f"{name} bucket {bucket}: inputs generated in {time.perf_counter() - t0:.1f} s")
         res = {}
-        energy, lse, _ = cba.calib_block_energy(qc, kc, None, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid)
-        e_ms = timed(lambda: cba.calib_block_energy(qc, kc, None, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid,
-                                                   lse=lse, energy=energy))
-        cal_flops = 4 * n * n * d * H * cfg.calib_draws  # QK^T in both sweeps
+        ws = torch.empty(cba.energy_workspace_bytes(qc, B), dtype=torch.uint8, device="cuda")
+        energy, lse, _ = cba.calib_block_energy_ws(qc, kc, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid, workspace=ws)
+        e_ms = timed(lambda: cba.calib_block_energy_ws(qc, kc, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid,
+                                                      workspace=ws, lse=lse, energy=energy))
+        del ws
+        e2, l2, _ = cba.calib_block_energy(qc, kc, None, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid)
+        e2_ms = timed(lambda: cba.calib_block_energy(qc, kc, None, block=B, n_prefix=cfg.n_prefix, grid=cfg.grid,
+                                                    lse=l2, energy=e2))
+        e2_diff = float((e2 - energy).abs().max())
+        del e2, l2
+        cal_flops = 2 * n * n * d * H * cfg.calib_draws  # QK^T, once per draw
         tau = cfg.tau if tau_schedule is None else tau_schedule[min(bucket, len(tau_schedule) - 1)]
         mask = cba.select_blocks_by_energy(energy, tau, cfg.rho, True, cfg.n_prefix_blocks)
         s_ms = timed(lambda: cba.select_blocks_by_energy(energy, tau, cfg.rho, True, cfg.n_prefix_blocks,
@@ -282,7 +290,8 @@ def calibrated_workload(name, reps=2, tau_schedule=None):
         kept = kept_flops(m, cfg, np.zeros(H, bool), (rows_per_block(cfg, False),) * 2)
         dens = m.mean(axis=(1, 2))
         res.update({"bucket": bucket, "tau": tau, "draws": cfg.calib_draws, "calib_ms": e_ms,
-                    "calib_tflops": cal_flops / e_ms / 1e9, "select_ms": s_ms, "csr_ms": c_ms,
+                    "calib_tflops": cal_flops / e_ms / 1e9, "calib_two_sweep_ms": e2_ms,
+                    "calib_two_sweep_max_abs_diff": e2_diff, "select_ms": s_ms, "csr_ms": c_ms,
                     "mask_density": float(m.mean()), "head_density_min": float(dens.min()),
                     "head_density_max": float(dens.max()), "order_ms": o_ms, "sparse_natural_order_ms": spn_ms,
                     "sparse_ms": sp_ms, "sparse_tflops": kept / sp_ms / 1e9,
@@ -290,7 +299,8 @@ def calibrated_workload(name, reps=2, tau_schedule=None):
                     "intervals_build_ms": ivb_ms, "sparse_intervals_ms": iv_ms, "intervals_same_output": same,
                     "runs": n_runs, "kept_blocks": int(m.sum()),
                     "skip_list_bytes": skip_list_bytes(H * cfg.nb, cfg.nb, int(m.sum()), n_runs)})
-        log(f"{name} bucket {bucket}: calibration {e_ms:.1f} ms ({res['calib_tflops']:.0f} TFLOP/s), select "
+        log(f"{name} bucket {bucket}: calibration {e_ms:.1f} ms ({res['calib_tflops']:.0f} TFLOP/s; two sweeps "
+            f"{e2_ms:.1f} ms, max |dE| {e2_diff:.1e}), select "
             f"{s_ms:.2f} ms, density {res['mask_density']:.3f}, sparse {sp_ms:.2f} ms (natural order {spn_ms:.2f}) "
             f"({res['sparse_tflops']:.0f} TFLOP/s kept), dense {de_ms:.2f} ms; intervals: {n_runs} runs for "
             f"{int(m.sum())} blocks, sparse {iv_ms:.2f} ms")
@@ -302,12 +312,13 @@ def calibrated_workload(name, reps=2, tau_schedule=None):
 
 def online_search(name, n_steps=8, search_steps=(0, 4)):
     """Online search on one workload (the search-and-reuse schedule of AdaSpa's
-    method): at step 0 a fused dense pass gives the step's output and caches the LSE,
-    then energies, selection and the skip list; the following steps reuse the mask
+    method): at step 0 one dense pass (calib_block_energy_ws) gives the step's output,
+    the LSE and the energies, then selection and the skip list; the following steps reuse the mask
     with sparse attention; at each later search step the output comes from the
-    current mask and the energies from an LSE without a dense pass: either the one
-    cached at step 0 (the pages' reuse of the cache), or the LSE that the step's own
-    sparse pass writes over its kept blocks.  Each step's input is a fresh seeded
+    current mask and the energies from: the LSE cached at step 0 (the pages' reuse of
+    the cache), the LSE that the step's own sparse pass writes over its kept blocks,
+    or the step's own full LSE, which the one-pass sweep without V computes along with
+    the energies ("own": the same mask as a search with a dense pass).  Each step's input is a fresh seeded
     draw of the workload.  Reports per-step times against dense attention, the output
     error against dense at every step, and the mask agreement of each later search
     with a search from the step's own dense LSE."""
@@ -344,7 +355,8 @@ def online_search(name, n_steps=8, search_steps=(0, 4)):
             own_masks[st] = cba.select_blocks_by_energy_heads(e_own, taus, cfg.rho, True, cfg.n_prefix_blocks)
             del e_own
     out = {"search_steps": list(search_steps), "tau": cfg.tau, "dense_ms": dense_ms}
-    for source in ("cached", "sparse"):
+    ws = torch.empty(cba.energy_workspace_bytes(o, B), dtype=torch.uint8, device="cuda")
+    for source in ("cached", "sparse", "own"):
         lse = None
         row_ptr = col_idx = None
         steps = []
@@ -354,10 +366,13 @@ def online_search(name, n_steps=8, search_steps=(0, 4)):
             torch.cuda.synchronize()
             a.record()
             if st == 0:
-                energy, lse, _ = cba.calib_block_energy(q, k, v, o=o, **kw)
+                energy, lse, _ = cba.calib_block_energy_ws(q, k, v, o=o, workspace=ws, **kw)
             elif search and source == "sparse":
                 cba.sparse_attn_fwd(q, k, v, row_ptr, col_idx, o=o, lse=lse_now, **kw)
                 energy = cba.block_energy_from_lse(q, k, lse_now, **kw)
+            elif search and source == "own":
+                cba.sparse_attn_fwd(q, k, v, row_ptr, col_idx, o=o, **kw)
+                energy, _, _ = cba.calib_block_energy_ws(q, k, workspace=ws, lse=lse_now, **kw)
             else:
                 cba.sparse_attn_fwd(q, k, v, row_ptr, col_idx, o=o, **kw)
                 if search:
@@ -544,6 +559,22 @@ def main():
         eo = torch.empty_like(qd)
         en_ms = timeit(lambda: cba.calib_block_energy(qd, kd, vd, block=B, lse=lse, energy=energy, o=eo), reps=2)
         rows["calib_block_energy"] = {"ms": en_ms, "draws": 1, "tflops": 1.5 * dense_flops / en_ms / 1e9}
+        # energies, LSE and O in one sweep over the keys, with its workspace; also without V
+        ws = torch.empty(cba.energy_workspace_bytes(qd, B), dtype=torch.uint8, device="cuda")
+        e1, l1, o1 = torch.empty_like(energy), torch.empty_like(lse), torch.empty_like(eo)
+        e1_ms = timeit(lambda: cba.calib_block_energy_ws(qd, kd, vd, block=B, workspace=ws, lse=l1, energy=e1,
+                                                         o=o1), reps=2)
+        same_o = bool(torch.equal(o1, eo)) and bool(torch.equal(l1, lse))
+        e1k_ms = timeit(lambda: cba.calib_block_energy_ws(qd, kd, block=B, workspace=ws, lse=l1, energy=e1), reps=2)
+        rows["calib_block_energy_ws"] = {"ms": e1_ms, "draws": 1, "tflops": dense_flops / e1_ms / 1e9,
+                                         "without_v_ms": e1k_ms,
+                                         "without_v_tflops": 0.5 * dense_flops / e1k_ms / 1e9,
+                                         "workspace_bytes": ws.numel(), "o_lse_same_as_two_sweep": same_o,
+                                         "max_abs_diff_vs_two_sweep": float((e1 - energy).abs().max())}
+        log(f"calib_block_energy_ws {e1_ms:.2f} ms ({dense_flops / e1_ms / 1e9:.0f} TFLOP/s; two sweeps "
+            f"{en_ms:.2f} ms); without V {e1k_ms:.2f} ms; O and LSE identical {same_o}, max |dE| "
+            f"{rows['calib_block_energy_ws']['max_abs_diff_vs_two_sweep']:.2e}")
+        del ws, e1, l1, o1
         sel_ms = timeit(lambda: cba.select_blocks_by_energy(energy, 0.95, 0.5))
         rows["select_blocks_by_energy"] = {"ms": sel_ms, "draws": 1}
         # repetition detection on the same draw, from the LSE of the energy pass

@@ -128,14 +128,14 @@ def energy_workspace_bytes(q: torch.Tensor, block: int) -> int:
     return b * h * nb * nb * block * 4
 
 
-def calib_block_energy_ws(q, k, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,
+def calib_block_energy_ws(q, k, v=None, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,
                           workspace: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          energy: Optional[torch.Tensor] = None):
-    """Energies and LSE in one pass over the keys (no V), using a workspace of
+                          energy: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None):
+    """calib_block_energy in one pass over the keys, using a workspace of
     energy_workspace_bytes(q, block) bytes (allocated here when not given).
-    Returns (energy, lse)."""
-    _require_gpu(q, k, workspace, lse, energy)
-    _same_layout(q, k)
+    Returns (energy, lse, o); o is None without v."""
+    _require_gpu(q, k, v, workspace, lse, energy, o)
+    _same_layout(q, k, v, o)
     desc = make_desc(q, block, n_prefix, grid, scale)
     b, h, n, _ = q.shape
     nb = n_blocks(n, block)
@@ -143,15 +143,18 @@ def calib_block_energy_ws(q, k, *, block: int, n_prefix: int = 0, grid=None, sca
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     if energy is None:
         energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
+    if v is not None and o is None:
+        o = torch.empty_like(q)
     need = energy_workspace_bytes(q, block)
     if workspace is None:
         workspace = torch.empty(need if q.dtype == torch.bfloat16 else 16, dtype=torch.uint8, device=q.device)
     if not (lse.is_contiguous() and energy.is_contiguous() and workspace.is_contiguous()):
         raise CalibAttnError("lse, energy and workspace must be contiguous")
-    _check(_lib.load().calib_block_energy_ws(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(energy),
-                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                             _stream()), "calib_block_energy_ws")
-    return energy, lse
+    _check(_lib.load().calib_block_energy_ws(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                             _ptr(energy), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream()),
+           "calib_block_energy_ws")
+    return energy, lse, o
 
 
 def block_energy_from_lse(q, k, lse, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,

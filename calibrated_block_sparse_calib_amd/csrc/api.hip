@@ -119,22 +119,26 @@ CBA_API cba_status calib_block_energy(const cba_attn_desc* desc, const void* q, 
   return from_hip(e);
 }
 
-CBA_API cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* q, const void* k, float* lse,
-                                         float* energy, void* workspace, int64_t workspace_bytes,
-                                         cba_stream_t stream) {
+CBA_API cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* q, const void* k, const void* v,
+                                         void* o, float* lse, float* energy, void* workspace,
+                                         int64_t workspace_bytes, cba_stream_t stream) {
   cba_status st = check_desc(desc);
   if (st) return st;
   if (check_tensor(q) || check_tensor(k) || !lse || !energy) return CBA_EINVAL;
+  if ((v == nullptr) != (o == nullptr)) return CBA_EINVAL;
+  if (v && (check_tensor(v) || check_tensor(o))) return CBA_EINVAL;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(energy) & 3u)) return CBA_EINVAL;
   AttnParams p = make_params(desc);
   p.q = q;
   p.k = k;
+  p.v = v;
+  p.o = o;
   p.lse = lse;
   p.energy = energy;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (desc->dtype != CBA_DTYPE_BF16) {
     // fp32: the two sweeps (no workspace needed).
-    hipError_t e = run_attention(p, desc, /*with_pv=*/false, s);
+    hipError_t e = run_attention(p, desc, /*with_pv=*/v != nullptr, s);
     if (e != hipSuccess) return from_hip(e);
     return from_hip(cba::launch_energy_f32(p, desc->head_dim, desc->block, s));
   }

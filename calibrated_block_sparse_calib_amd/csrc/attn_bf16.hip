@@ -477,11 +477,15 @@ hipError_t launch_attn_t(const AttnParams& p, bool with_pv, hipStream_t stream) 
 // one wave per (query block, key block) pair at a time, in a fixed order, so the
 // result does not depend on QPB.  Workspace layout: [batch, heads, nb (qb), nb (kb),
 // B] floats, so the rows of one (qb, kb) are contiguous.
-template <int D, int B, int QPB, bool BUF>
+// PV: the pass also multiplies by V and writes O, step for step as attn_item's
+// dense pass (same weights, same order), so O and the LSE are those of
+// dense_attn_fwd bit for bit.
+template <int D, int B, int QPB, bool PV, bool BUF>
 __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(AttnParams p, float* ws) {
   using C = Cfg<D, B>;
   constexpr int NW = QPB * C::NW;  // waves per workgroup, 32 rows each
   __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bfraw v0s[PV ? C::TILE : 8], v1s[PV ? C::TILE : 8];
   __shared__ float lse2_s[QPB * B];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
@@ -495,6 +499,7 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
   const int64_t head_off = (int64_t)b * p.sb + (int64_t)h * p.sh;
   const bfraw* qg = static_cast<const bfraw*>(p.q) + head_off;
   const bfraw* kg = static_cast<const bfraw*>(p.k) + head_off;
+  const bfraw* vg = PV ? static_cast<const bfraw*>(p.v) + head_off : nullptr;
   const int qi = wave * 32 + (lane & 31);
   const bool wave_active = wave * 32 < M;
   const bool q_valid = qi < M;
@@ -520,22 +525,33 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
   if (BUF) tile_lane_offsets<D, C::KT, NW>((int)(p.sn * 2), voff);
   const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto load = [&](int k0, bfraw* kdst) {
-    if (BUF) load_tile_buf(kg, nrec, voff, LPW, k0 * (int)(p.sn * 2), kdst + wv * LPW * 512);
-    else load_tile<D, C::KT, NW>(kg, p.sn, p.n, k0, kdst);
+  auto load = [&](int k0, bfraw* kdst, bfraw* vdst) {
+    if (BUF) {
+      const int so = k0 * (int)(p.sn * 2);
+      load_tile_buf(kg, nrec, voff, LPW, so, kdst + wv * LPW * 512);
+      if (PV) load_tile_buf(vg, nrec, voff, LPW, so, vdst + wv * LPW * 512);
+    } else {
+      load_tile<D, C::KT, NW>(kg, p.sn, p.n, k0, kdst);
+      if (PV) load_tile<D, C::KT, NW>(vg, p.sn, p.n, k0, vdst);
+    }
   };
+  f32x16 oacc[PV ? C::DT : 1];
+#pragma unroll
+  for (int dt = 0; dt < (PV ? C::DT : 1); ++dt) oacc[dt] = f32x16{};
   float m_used = -INFINITY;  // reference maximum, base-2 units
   float l_part = 0.f;        // this lane's share of the row sum
   float b_part = 0.f;        // this lane's share of the current key block's sum
+  float r_part = 0.f;        // this lane's share of the rounded-weight sum (O)
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   int k0_cur = step_key0(0);
-  load(k0_cur, k0s);
-  auto step = [&](int s, const bfraw* kt, bfraw* kn) {
+  load(k0_cur, k0s, v0s);
+  auto step = [&](int s, const bfraw* kt, const bfraw* vt, bfraw* kn, bfraw* vn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int k0_next = -1;
     if (s + 1 < nsteps) {
       k0_next = step_key0(s + 1);
-      load(k0_next, kn);
+      load(k0_next, kn, vn);
     }
     if (wave_active && k0_cur >= 0) {
       f32x16 sacc[C::ST];
@@ -576,15 +592,54 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
         const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
         l_part *= alpha;
         b_part *= alpha;
+        if (PV) {
+          r_part *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        }
         m_used = m_new;
       }
+      bf16x8 pb[PV ? C::ST : 1][2];
       float ps = 0.f;
 #pragma unroll
       for (int t = 0; t < C::ST; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], p.c, -m_used));
+        for (int i = 0; i < 16; ++i) {
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], p.c, -m_used));
+          ps += x;
+          if (PV) pb[t][i >> 3][i & 7] = (__bf16)x;
+        }
       l_part += ps;
       b_part += ps;
+      if (PV) {
+        // O^T += V^T P^T, normalised at the end by the sum of the rounded weights.
+#pragma unroll
+        for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2 pair = {pb[t][k2][e], pb[t][k2][e + 1]};
+              r_part = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, r_part, false);
+            }
+        const int G = lane >> 4, li = lane & 15;
+#pragma unroll
+        for (int t = 0; t < C::ST; ++t)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int krow = t * 32 + k2 * 16 + 4 * g + (li >> 2);
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+              const int dcol = dt * 32 + (G & 1) * 16 + 4 * (li & 3);
+              const i16x4 lo = lds_read_tr(vt + tile_off<D>(krow, dcol));
+              const i16x4 hi = lds_read_tr(vt + tile_off<D>(krow + 8, dcol));
+              const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              oacc[dt] = mfma(va, pb[t][k2], oacc[dt]);
+            }
+          }
+      }
     }
     if (s % C::SPB == C::SPB - 1) {
       // End of key block s / SPB: its base-2 log-sum for this lane's row.
@@ -596,10 +651,10 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
   };
   int s = 0;
   for (; s + 1 < nsteps; s += 2) {
-    step(s, k0s, k1s);
-    step(s + 1, k1s, k0s);
+    step(s, k0s, v0s, k1s, v1s);
+    step(s + 1, k1s, v1s, k0s, v0s);
   }
-  if (s < nsteps) step(s, k0s, k1s);
+  if (s < nsteps) step(s, k0s, v0s, k1s, v1s);
 
   // Row log-sum-exp: LSE output (natural log) and, for the reduction, base 2.
   if (wave_active) {
@@ -608,6 +663,22 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
     if (g == 0) {
       lse2_s[qi] = q_valid ? lse2 : INFINITY;  // rows past the end add nothing
       if (q_valid) p.lse[bh * p.n + qtok] = lse2 * kLn2;
+    }
+    if (PV) {
+      const float r_tot = r_part + other_half(r_part);
+      const float inv = r_tot > 0.f ? 1.f / r_tot : 0.f;
+      if (q_valid) {
+        bfraw* og = static_cast<bfraw*>(p.o) + head_off + (int64_t)qtok * p.sn;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[dt][r * 4 + e] * inv);
+            *reinterpret_cast<bf16x4*>(og + dt * 32 + r * 8 + g * 4) = w;
+          }
+      }
     }
   } else if (lane < 32) {
     lse2_s[qi] = INFINITY;
@@ -671,18 +742,24 @@ constexpr int energy1_qpb() {
   return energy_qpb<D, B>();
 }
 
-template <int D, int B>
-hipError_t launch_energy1_t(const AttnParams& p, float* ws, hipStream_t stream) {
+// With V: one query block per workgroup, as the dense pass.
+template <int D, int B, int Q, bool PV>
+hipError_t launch_energy1_q(const AttnParams& p, float* ws, hipStream_t stream) {
   using C = Cfg<D, B>;
-  constexpr int Q = energy1_qpb<D, B>();
   const int64_t nqg = (p.nb + Q - 1) / Q;
   const dim3 grid((unsigned)((int64_t)p.heads * nqg * p.batch)), block(Q * C::NT);
   const bool buf = (int64_t)(p.n + C::KT) * p.sn * 2 < ((int64_t)1 << 31);
-  auto kern = buf ? energy1_bf16_kernel<D, B, Q, true> : energy1_bf16_kernel<D, B, Q, false>;
+  auto kern = buf ? energy1_bf16_kernel<D, B, Q, PV, true> : energy1_bf16_kernel<D, B, Q, PV, false>;
   AttnParams arg = p;
   float* w = ws;
   void* args[] = {&arg, &w};
   return hipLaunchKernel((const void*)kern, grid, block, args, 0, stream);
+}
+
+template <int D, int B>
+hipError_t launch_energy1_t(const AttnParams& p, float* ws, hipStream_t stream) {
+  if (p.v) return launch_energy1_q<D, B, 1, true>(p, ws, stream);
+  return launch_energy1_q<D, B, energy1_qpb<D, B>(), false>(p, ws, stream);
 }
 
 }  // namespace

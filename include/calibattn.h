@@ -85,20 +85,23 @@ cba_status calib_block_energy(const cba_attn_desc* desc, const void* q, const vo
                               const void* v, void* o, float* lse, float* energy,
                               cba_stream_t stream);
 
-/* calib_block_energy without V in a single pass over the keys (bf16), with a
- * caller workspace instead of the second sweep.  For each row and key block the
- * pass stores the block's base-2 log-sum of the scaled scores in the workspace;
- * once the row's log-sum-exp is known the workgroup adds exp(.. - lse_i) of its
- * rows per block (zh S2.2A: E[qb, kb] = sum of the tile's attention
- * probabilities).  Outputs as calib_block_energy: lse (natural log) and energy,
- * each entry the sum of one tile in a fixed order (repeated calls give identical
- * bits; the bits may differ from calib_block_energy's by rounding).
+/* calib_block_energy in a single pass over the keys (bf16), with a caller
+ * workspace instead of the second sweep.  For each row and key block the pass
+ * stores the block's base-2 log-sum of the scaled scores in the workspace; once
+ * the row's log-sum-exp is known the workgroup adds exp(.. - lse_i) of its rows per
+ * block (zh S2.2A: E[qb, kb] = sum of the tile's attention probabilities).
+ * Arguments and outputs as calib_block_energy: v and o both NULL or both set; with
+ * V the pass also writes O.  lse and O are bit-identical to calib_block_energy's
+ * (and dense_attn_fwd's); each energy entry is the sum of one tile in a fixed
+ * order (repeated calls give identical bits; they may differ from
+ * calib_block_energy's by rounding).
  *   workspace: device, 16-byte aligned, at least batch * heads * nb * nb * block
  *              floats (workspace_bytes); its contents on entry do not matter and
  *              are left undefined.  CBA_ECAPACITY when too small.
  * fp32 inputs run the two sweeps and do not use the workspace. */
-cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* q, const void* k, float* lse,
-                                 float* energy, void* workspace, int64_t workspace_bytes, cba_stream_t stream);
+cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, float* energy, void* workspace, int64_t workspace_bytes,
+                                 cba_stream_t stream);
 
 /* Block energy sweep alone, from a given log-sum-exp ([AdaSpa] S2: the search pass
  * caches the LSE of its dense pass and later searches reuse that cache; zh S2.2A

@@ -203,10 +203,12 @@ def test_heavy_order_rejects_bad_arguments(lib):
 
 def test_energy_ws_rejects_bad_arguments(lib):
     d = _desc()  # bf16, 2 heads, 256 tokens, block 128: nb = 2, workspace 2*2*2*128*4 = 4096 bytes
-    assert lib.calib_block_energy_ws(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 4096, None) == EINVAL
-    assert lib.calib_block_energy_ws(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4095, None) == 4  # ECAPACITY
-    assert lib.calib_block_energy_ws(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, 4096, None) == EINVAL
-    assert lib.calib_block_energy_ws(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10004), 4096,
-                                     None) == EINVAL
-    assert lib.calib_block_energy_ws(ctypes.byref(_desc(block=48)), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
-                                     None) == EUNSUPPORTED
+    f = lib.calib_block_energy_ws
+    assert f(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, None, 4096, None) == EINVAL  # no workspace
+    assert f(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 4095, None) == 4  # ECAPACITY
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4095, None) == 4  # with V too
+    assert f(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE, 4096, None) == EINVAL  # no lse
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4096, None) == EINVAL  # v without o
+    assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == EINVAL  # o without v
+    assert f(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, ctypes.c_void_p(0x10004), 4096, None) == EINVAL
+    assert f(ctypes.byref(_desc(block=48)), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1 << 20, None) == EUNSUPPORTED

@@ -1,6 +1,8 @@
 """GPU parity of the one-pass energy sweep (calib_block_energy_ws) against the fp64
 oracle: energies |dE| <= 1e-4 * block (bf16), LSE within 1e-3, repeated calls
-bit-identical, and the workspace size enforced."""
+bit-identical, and the workspace size enforced.  With V, O and the LSE are
+bit-identical to calib_block_energy's dense pass and the energies to the one-pass
+result without V; O is also checked against the oracle (bf16 max 1e-2, mean 1e-3)."""
 import ctypes
 
 import numpy as np
@@ -10,7 +12,7 @@ import torch
 import calibrated_block_sparse_calib_amd as cba
 import oracle
 from workloads import AttnConfig, get_config, make_qkv
-from tests.gpu_util import assert_close_lse, log, to_host
+from tests.gpu_util import assert_close_lse, assert_close_out, log, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -31,16 +33,23 @@ def _cfg(d, block, grid, n_prefix, heads=3):
 def test_onepass_energy_matches_oracle(d, block, grid, n_prefix):
     cfg = _cfg(d, block, grid, n_prefix)
     log(f"one-pass energy d={d} B={block} grid={grid} prefix={n_prefix}")
-    draws = [make_qkv(cfg, draw=i, with_v=False) for i in range(2)]
+    draws = [make_qkv(cfg, draw=i) for i in range(2)]
     q = np.stack([x[0] for x in draws])
     k = np.stack([x[1] for x in draws])
-    qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
-    kd = torch.from_numpy(k).to(torch.bfloat16).cuda()
-    e1, l1 = cba.calib_block_energy_ws(qd, kd, block=block)
-    e1b, l1b = cba.calib_block_energy_ws(qd, kd, block=block)
+    v = np.stack([x[2] for x in draws]) * 0.5  # halved (exact): |o| stays below 4, where bf16 spacing reaches the bar
+    qd, kd, vd = (torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda() for x in (q, k, v))
+    e1, l1, _ = cba.calib_block_energy_ws(qd, kd, block=block)
+    e1b, l1b, _ = cba.calib_block_energy_ws(qd, kd, block=block)
     e2, l2, _ = cba.calib_block_energy(qd, kd, None, block=block)
+    ev, lv, ov = cba.calib_block_energy_ws(qd, kd, vd, block=block)
+    _, l2v, o2v = cba.calib_block_energy(qd, kd, vd, block=block)
     torch.cuda.synchronize()
     assert torch.equal(e1, e1b) and torch.equal(l1, l1b)
+    assert torch.equal(ov, o2v) and torch.equal(lv, l2v) and torch.equal(lv, l1)
+    assert torch.equal(ev, e1)
+    for dr in range(2):
+        refd, _ = oracle.dense_attention(q[dr, 0], k[dr, 0], v[dr, 0])
+        assert_close_out(to_host(ov)[dr, 0], refd, "bf16", f"one-pass O draw {dr}")
     got_e, got_l = to_host(e1), to_host(l1)
     worst = 0.0
     for dr in range(2):
@@ -74,7 +83,7 @@ def test_onepass_energy_full_size_hunyuan():
     q, k, _ = make_qkv(cfg, draw=0, with_v=False)
     qd = torch.from_numpy(q[None]).to(torch.bfloat16).cuda()
     kd = torch.from_numpy(k[None]).to(torch.bfloat16).cuda()
-    e1, l1 = cba.calib_block_energy_ws(qd, kd, block=cfg.block)
+    e1, l1, _ = cba.calib_block_energy_ws(qd, kd, block=cfg.block)
     e2, l2, _ = cba.calib_block_energy(qd, kd, None, block=cfg.block)
     torch.cuda.synchronize()
     assert float((e1 - e2).abs().max()) <= 2e-4 * cfg.block
