@@ -98,8 +98,9 @@ def traffic_from_profile():
     return t.get("bytes_per_launch") if t.get("source_hash") == source_hash() else None
 
 
-def cpu_baseline(cfg, q, k, v, mask, rep, got_o, budget_s, seed=0):
-    """Time the fp64 oracle on sampled query blocks of the same workload."""
+def cpu_baseline(cfg, q, k, v, mask, rep, got_o, budget_s, step_flops, seed=0):
+    """Time the fp64 oracle on sampled query blocks of the same workload; the time of
+    a whole step (step_flops kept FLOPs) is extrapolated from the sample's rate."""
     import oracle
 
     try:
@@ -133,6 +134,8 @@ def cpu_baseline(cfg, q, k, v, mask, rep, got_o, budget_s, seed=0):
         "cores": cores,
         "kind": "oracle",
         "sample": f"{done} query blocks ({done * B} rows max) of {cfg.name}, fp64 NumPy, {dt:.1f} s",
+        "sec_per_block": dt / done,
+        "extrapolated_step_s": step_flops / (flops / dt),  # by kept-work ratio, not measured
     }, {"rows_checked": int(err.shape[0]), "max_abs": float(err.max()), "mean_abs": float(err.mean())}
 
 
@@ -609,7 +612,7 @@ def main():
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cpu, parity = cpu_baseline(cfg, q, k, v, mask, rep, got_o, args.cpu_budget)
+        cpu, parity = cpu_baseline(cfg, q, k, v, mask, rep, got_o, args.cpu_budget, flops)
         log(f"cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} cores; sampled parity {parity}")
         if "spatial_rep_similarity" in rows:
             rows["spatial_rep_similarity"]["parity_sample"] = rep_sampled_parity(cfg, q, k, rep_tok_host)

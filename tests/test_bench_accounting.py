@@ -62,3 +62,26 @@ def test_more_than_one_gpu_is_refused():
                        stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_fields_and_extrapolation():
+    """The oracle timing leg on a small workload: every sampled block is compared with
+    an exact output (zero error), and the extrapolated step time is the step's kept
+    FLOPs over the sample's rate."""
+    cfg = _cfg()
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((cfg.heads, cfg.seq_len, cfg.head_dim)) for _ in range(3))
+    mask = (rng.random((cfg.heads, cfg.nb, cfg.nb)) < 0.5).astype(np.uint8)
+    for h in range(cfg.heads):
+        np.fill_diagonal(mask[h], 1)
+    rep = np.array([0, 1, 0], np.uint8)
+    got = np.stack([oracle.sparse_attention_with_repetition(q[h], k[h], v[h], mask[h], cfg.block, cfg.n_prefix,
+                                                            cfg.grid, cfg.anchor_stride, bool(rep[h]))[0]
+                    for h in range(cfg.heads)])
+    comp = (bench.rows_per_block(cfg, False), bench.rows_per_block(cfg, True))
+    step = bench.kept_flops(mask, cfg, rep, comp)
+    cpu, parity = bench.cpu_baseline(cfg, q, k, v, mask, rep, got, 0.5, step)
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "TFLOP/s" and cpu["cores"] >= 1
+    assert parity["max_abs"] <= 1e-12
+    assert abs(cpu["extrapolated_step_s"] * cpu["value"] * 1e12 - step) <= 1e-6 * step
+    assert cpu["sec_per_block"] > 0
