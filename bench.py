@@ -72,8 +72,8 @@ KERNEL_UNIT = ("attn_bf16.hip", "mfma_util.h")  # the sparse kernel's own source
 
 def source_hash():
     """Hash of the sources compiled into the sparse kernel (its file, the device
-    helpers, and the parameter block it reads from the shared header): byte
-    counters taken on another version of them are not reported."""
+    helpers, its compile flags and the parameter block it reads from the shared
+    header): byte counters taken on another version of them are not reported."""
     import re
 
     h = hashlib.sha256()
@@ -81,6 +81,9 @@ def source_hash():
     for name in KERNEL_UNIT:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
+    from calibrated_block_sparse_calib_amd.build import EXTRA
+
+    h.update(" ".join(EXTRA.get(KERNEL_UNIT[0], [])).encode())  # its compile flags
     with open(os.path.join(csrc, "cba_internal.h")) as f:
         hdr = f.read()
     for pat in (r"struct AttnParams \{.*?\n\};", r"inline bool rep_head\(.*?\n\}", r"constexpr int kMaxRepHeads = \d+;"):

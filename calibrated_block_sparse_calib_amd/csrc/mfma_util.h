@@ -14,6 +14,30 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t bfraw;
 #define LDS_AS __attribute__((address_space(3)))
 
+// Tile configuration of the bf16 attention-shaped kernels: B query rows per work
+// item in waves of 32 rows, K and V staged in KT-key steps.
+template <int D, int B>
+struct Cfg {
+  static constexpr int NW = B / 32;              // waves, 32 query rows each
+  static constexpr int NT = NW * 64;             // threads
+  static constexpr int KT = B < 64 ? B : 64;     // keys per step
+  static constexpr int SPB = B / KT;             // steps per key block
+  static constexpr int TILE = KT * D;            // elements per K or V tile
+  static constexpr int KS = D / 16;              // k-steps of the QK^T product
+  static constexpr int DT = D / 32;              // 32-wide d tiles of O
+  static constexpr int ST = KT / 32;             // 32-key score tiles per step
+};
+
+// Query blocks per energy workgroup: about 256 query rows (8 waves) share each K
+// tile, as far as the tile splits over the waves.
+template <int D, int B>
+constexpr int energy_qpb() {
+  using C = Cfg<D, B>;
+  constexpr int max_waves = C::KT * D / 512;  // one 1 KB tile load per wave at least
+  constexpr int waves = max_waves < 8 ? max_waves : 8;
+  return waves / C::NW > 0 ? waves / C::NW : 1;
+}
+
 // The online softmax rescales its output only when a row maximum grows by more
 // than this many units of log2: the weights stay below 2^8, which bf16 and the
 // fp32 accumulators hold exactly as well as weights below 1.
