@@ -16,7 +16,10 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libcalibattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "attn_bf16.hip", "energy1_bf16.hip", "attn_f32.hip", "select_csr.hip", "repetition.hip"]
+SOURCES = [
+    "api.hip", "attn_bf16.hip", "energy1_bf16.hip", "energy1_o_bf16.hip", "attn_f32.hip", "select_csr.hip",
+    "repetition.hip",
+]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -48,13 +51,16 @@ def _run(cmd):
 # Per-source extra flags.  The bf16 kernels assume no NaN inputs, so maxima skip
 # the NaN-quieting the IEEE mode would otherwise add before every comparison;
 # the host-side validation (isfinite checks) lives in api.hip, built without it.
-# The attention kernels are scheduled with LLVM's iterative ILP strategy, which
-# measured 1-2% faster on sparse and dense attention and the energy sweep; the
-# one-pass energy kernel with V measured 7% slower with it, so it lives in its own
-# file with the default strategy.
+# The attention kernels and the one-pass energy kernel without V are scheduled
+# with LLVM's iterative ILP strategy, which measured 1-3% faster on sparse and
+# dense attention and on both energy passes without V; the one-pass energy kernel
+# with V measured 7-8% slower with it, so its instantiation has a file of its own
+# with the default strategy.
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 EXTRA = {
-    "attn_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-    "energy1_bf16.hip": ["-fno-honor-nans"],
+    "attn_bf16.hip": ["-fno-honor-nans", *_ILP],
+    "energy1_bf16.hip": ["-fno-honor-nans", *_ILP],
+    "energy1_o_bf16.hip": ["-fno-honor-nans"],
 }
 
 

@@ -86,8 +86,10 @@ inline int64_t rep_grid(int batch, int heads, int gf, int gh, int gw, int stride
 // block when p.row_ptr is null (dense).  with_pv = false computes only the LSE.
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block, bool with_pv, hipStream_t stream);
 hipError_t launch_energy_bf16(const AttnParams& p, int head_dim, int block, hipStream_t stream);
-// One-pass energies with the per-(row, key block) log-sums in ws [batch, heads, nb, nb, block].
+// One-pass energies with the per-(row, key block) log-sums in ws [batch, heads, nb, nb, block]
+// (O too when p.v is set; the _k variant is the case without V).
 hipError_t launch_energy1_bf16(const AttnParams& p, int head_dim, int block, float* ws, hipStream_t stream);
+hipError_t launch_energy1_k_bf16(const AttnParams& p, int head_dim, int block, float* ws, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, int block, bool with_pv, hipStream_t stream);
 hipError_t launch_energy_f32(const AttnParams& p, int head_dim, int block, hipStream_t stream);
 hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, const TauTable& taus, double rho,
