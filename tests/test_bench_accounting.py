@@ -85,3 +85,26 @@ def test_cpu_baseline_fields_and_extrapolation():
     assert parity["max_abs"] <= 1e-12
     assert abs(cpu["extrapolated_step_s"] * cpu["value"] * 1e12 - step) <= 1e-6 * step
     assert cpu["sec_per_block"] > 0
+
+
+def test_traffic_figure_is_tied_to_the_kernel_build(monkeypatch, tmp_path):
+    """The stored byte-counter figure is reported only for the sources and compile
+    flags it was measured on: a change to either changes the hash, and a stored
+    figure with another hash reads as unmeasured (None)."""
+    from calibrated_block_sparse_calib_amd import build
+
+    h0 = bench.source_hash()
+    assert h0 == bench.source_hash()  # deterministic
+    flags = dict(build.EXTRA)
+    flags[bench.KERNEL_UNIT[0]] = list(flags.get(bench.KERNEL_UNIT[0], [])) + ["-DSOME_OTHER_BUILD"]
+    monkeypatch.setattr(build, "EXTRA", flags)
+    assert bench.source_hash() != h0
+    monkeypatch.setattr(build, "EXTRA", dict(build.EXTRA, **{bench.KERNEL_UNIT[0]: []}))
+    assert bench.source_hash() != h0
+    monkeypatch.undo()
+    stored = tmp_path / "traffic.json"
+    stored.write_text('{"source_hash": "%s", "bytes_per_launch": 123}' % h0)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stored))
+    assert bench.traffic_from_profile() == 123
+    stored.write_text('{"source_hash": "0000000000000000", "bytes_per_launch": 123}')
+    assert bench.traffic_from_profile() is None
