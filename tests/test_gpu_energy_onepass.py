@@ -29,6 +29,7 @@ def _cfg(d, block, grid, n_prefix, heads=3):
     (64, 128, (1, 13, 12), 128),
     (128, 64, (2, 8, 8), 0),      # exact multiple
     (128, 128, (1, 1, 5), 0),     # one short block
+    (64, 32, (2, 5, 7), 32),      # ragged last block of 6, text prefix
 ])
 def test_onepass_energy_matches_oracle(d, block, grid, n_prefix):
     cfg = _cfg(d, block, grid, n_prefix)
