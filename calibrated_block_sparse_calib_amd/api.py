@@ -65,6 +65,15 @@ def _same_layout(ref: torch.Tensor, *ts):
             raise CalibAttnError("q, k, v and o must share shape, strides and dtype")
 
 
+def _check_out(t: Optional[torch.Tensor], shape, dtype, name: str):
+    """A caller-supplied buffer the library writes (or reads) by pointer alone: its
+    dtype, shape and contiguity must be exactly the documented ones."""
+    if t is None:
+        return
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise CalibAttnError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
 def _rep_array(rep_heads, heads):
     if rep_heads is None:
         return None, None
@@ -83,19 +92,19 @@ def calib_block_energy(q, k, v=None, *, block: int, n_prefix: int = 0, grid=None
                        o: Optional[torch.Tensor] = None):
     """Dense pass (LSE cached, O when v is given) then block energies.
     The batch index is the calibration draw.  Returns (energy, lse, o)."""
-    _require_gpu(q, k, v)
-    _same_layout(q, k, v)
+    _require_gpu(q, k, v, lse, energy, o)
+    _same_layout(q, k, v, o)
     desc = make_desc(q, block, n_prefix, grid, scale)
     b, h, n, _ = q.shape
     nb = n_blocks(n, block)
+    _check_out(lse, (b, h, n), torch.float32, "lse")
+    _check_out(energy, (b, h, nb, nb), torch.float32, "energy")
     if lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     if energy is None:
         energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
     if v is not None and o is None:
         o = torch.empty_like(q)
-    if not (lse.is_contiguous() and energy.is_contiguous()):
-        raise CalibAttnError("lse and energy must be contiguous")
     _check(_lib.load().calib_block_energy(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                           _ptr(lse), _ptr(energy), _stream()), "calib_block_energy")
     return energy, lse, o
@@ -111,6 +120,9 @@ def select_blocks_by_energy(energy: torch.Tensor, tau: float, rho: float = 0.5, 
     d, h, nb, nb2 = energy.shape
     if nb != nb2:
         raise CalibAttnError("energy must be square per head")
+    _require_gpu(mask, votes)
+    _check_out(mask, (h, nb, nb), torch.uint8, "mask")
+    _check_out(votes, (h, nb, nb), torch.int32, "votes")
     if mask is None:
         mask = torch.empty((h, nb, nb), dtype=torch.uint8, device=energy.device)
     if return_votes and votes is None:
@@ -139,6 +151,8 @@ def calib_block_energy_ws(q, k, v=None, *, block: int, n_prefix: int = 0, grid=N
     desc = make_desc(q, block, n_prefix, grid, scale)
     b, h, n, _ = q.shape
     nb = n_blocks(n, block)
+    _check_out(lse, (b, h, n), torch.float32, "lse")
+    _check_out(energy, (b, h, nb, nb), torch.float32, "energy")
     if lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     if energy is None:
@@ -148,8 +162,8 @@ def calib_block_energy_ws(q, k, v=None, *, block: int, n_prefix: int = 0, grid=N
     need = energy_workspace_bytes(q, block)
     if workspace is None:
         workspace = torch.empty(need if q.dtype == torch.bfloat16 else 16, dtype=torch.uint8, device=q.device)
-    if not (lse.is_contiguous() and energy.is_contiguous() and workspace.is_contiguous()):
-        raise CalibAttnError("lse, energy and workspace must be contiguous")
+    if not workspace.is_contiguous():
+        raise CalibAttnError("workspace must be contiguous")
     _check(_lib.load().calib_block_energy_ws(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                              _ptr(energy), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream()),
@@ -170,8 +184,7 @@ def block_energy_from_lse(q, k, lse, *, block: int, n_prefix: int = 0, grid=None
         raise CalibAttnError("lse must be contiguous fp32 [batch, heads, seq_len]")
     if energy is None:
         energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
-    if not energy.is_contiguous() or energy.numel() != b * h * nb * nb:
-        raise CalibAttnError("energy must be contiguous fp32 [batch, heads, nb, nb]")
+    _check_out(energy, (b, h, nb, nb), torch.float32, "energy")
     _check(_lib.load().block_energy_from_lse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(energy),
                                              _stream()), "block_energy_from_lse")
     return energy
@@ -191,6 +204,9 @@ def select_blocks_by_energy_heads(energy: torch.Tensor, tau_heads, rho: float = 
     taus = np.ascontiguousarray(np.asarray(tau_heads, dtype=np.float64).reshape(-1))
     if taus.shape[0] != h:
         raise CalibAttnError("tau_heads needs one threshold per head")
+    _require_gpu(mask, votes)
+    _check_out(mask, (h, nb, nb), torch.uint8, "mask")
+    _check_out(votes, (h, nb, nb), torch.int32, "votes")
     if mask is None:
         mask = torch.empty((h, nb, nb), dtype=torch.uint8, device=energy.device)
     if return_votes and votes is None:
@@ -239,8 +255,8 @@ def order_heavy_rows_first(row_ptr: torch.Tensor, nkb: int, factor: float = 2.0,
     rows = row_ptr.numel() - 1
     if work_order is None:
         work_order = torch.empty(rows, dtype=torch.int32, device=row_ptr.device)
-    if work_order.dtype != torch.int32 or work_order.numel() != rows:
-        raise CalibAttnError("work_order must be int32 [rows]")
+    if work_order.dtype != torch.int32 or work_order.numel() != rows or not work_order.is_contiguous():
+        raise CalibAttnError("work_order must be contiguous int32 [rows]")
     _check(_lib.load().order_heavy_rows_first(_ptr(row_ptr), rows, int(nkb), float(factor), _ptr(work_order),
                                               _stream()), "order_heavy_rows_first")
     return work_order
@@ -284,14 +300,18 @@ def sparse_attn_fwd_intervals(q, k, v, iv_ptr, ivs, *, block: int, work_order=No
     _same_layout(q, k, v, o)
     desc = make_desc(q, block, n_prefix, grid, scale)
     b, h, n, _ = q.shape
+    _check_out(lse, (b, h, n), torch.float32, "lse")
     if return_lse and lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     if iv_ptr.dtype != torch.int32 or ivs.dtype not in (torch.int32, torch.uint32):
         raise CalibAttnError("iv_ptr must be int32 and ivs 32-bit")
+    if not (iv_ptr.is_contiguous() and ivs.is_contiguous()):
+        raise CalibAttnError("iv_ptr and ivs must be contiguous")
     if iv_ptr.numel() != h * n_blocks(n, block) + 1:
         raise CalibAttnError("iv_ptr must have heads * nb + 1 entries")
-    if work_order is not None and (work_order.dtype != torch.int32 or work_order.numel() != h * n_blocks(n, block)):
-        raise CalibAttnError("work_order must be int32 [heads * nb]")
+    if work_order is not None and (work_order.dtype != torch.int32 or work_order.numel() != h * n_blocks(n, block)
+                                   or not work_order.is_contiguous()):
+        raise CalibAttnError("work_order must be contiguous int32 [heads * nb]")
     rep_arr, rep_ptr = _rep_array(rep_heads, h)
     _check(_lib.load().sparse_attn_fwd_intervals(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(iv_ptr),
                                                  _ptr(ivs), ivs.numel(), _ptr(work_order), rep_ptr,
@@ -313,14 +333,18 @@ def sparse_attn_fwd(q, k, v, row_ptr, col_idx, *, block: int, work_order=None, r
     _same_layout(q, k, v, o)
     desc = make_desc(q, block, n_prefix, grid, scale)
     b, h, n, _ = q.shape
+    _check_out(lse, (b, h, n), torch.float32, "lse")
     if return_lse and lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
         raise CalibAttnError("row_ptr and col_idx must be int32")
+    if not (row_ptr.is_contiguous() and col_idx.is_contiguous()):
+        raise CalibAttnError("row_ptr and col_idx must be contiguous")
     if row_ptr.numel() != h * n_blocks(n, block) + 1:
         raise CalibAttnError("row_ptr must have heads * nb + 1 entries")
-    if work_order is not None and (work_order.dtype != torch.int32 or work_order.numel() != h * n_blocks(n, block)):
-        raise CalibAttnError("work_order must be int32 [heads * nb]")
+    if work_order is not None and (work_order.dtype != torch.int32 or work_order.numel() != h * n_blocks(n, block)
+                                   or not work_order.is_contiguous()):
+        raise CalibAttnError("work_order must be contiguous int32 [heads * nb]")
     rep_arr, rep_ptr = _rep_array(rep_heads, h)
     _check(_lib.load().sparse_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
                                        col_idx.numel(), _ptr(work_order), rep_ptr, int(anchor_stride),
@@ -351,6 +375,7 @@ def dense_attn_fwd(q, k, v, *, block: int = 128, scale: float = 0.0, o: Optional
     _same_layout(q, k, v, o)
     desc = make_desc(q, block, 0, None, scale)
     b, h, n, _ = q.shape
+    _check_out(lse, (b, h, n), torch.float32, "lse")
     if return_lse and lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     _check(_lib.load().dense_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream()),
@@ -393,8 +418,8 @@ def select_rep_heads(head_sim: torch.Tensor, gamma: float, rep_heads: Optional[t
     d, h = head_sim.shape
     if rep_heads is None:
         rep_heads = torch.empty(h, dtype=torch.uint8, device=head_sim.device)
-    if rep_heads.dtype != torch.uint8 or rep_heads.numel() != h:
-        raise CalibAttnError("rep_heads must be uint8 [heads]")
+    if rep_heads.dtype != torch.uint8 or rep_heads.numel() != h or not rep_heads.is_contiguous():
+        raise CalibAttnError("rep_heads must be contiguous uint8 [heads]")
     _check(_lib.load().select_rep_heads(_ptr(head_sim), d, h, float(gamma), _ptr(rep_heads), _stream()),
            "select_rep_heads")
     return rep_heads
