@@ -4,6 +4,8 @@ from a fixed seed per case, so that corners no hand-picked case covers get
 exercised.  Bars as elsewhere: bf16 max 1e-2 / mean 1e-3, fp32 max 1e-5, energies
 1e-4 * block (1e-5 * block in fp32), repetition cosines 1e-4 (1e-5 in fp32),
 integer results bit-exact."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,7 @@ from tests.gpu_util import assert_close_out, log, to_host
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = int(os.environ.get("CBA_RANDOM_CASES", "24"))  # more cases for an occasional wider sweep
 
 
 def _case(seed):
@@ -61,6 +63,7 @@ def test_random_shape(seed):
     o = cba.sparse_attn_fwd(qd, kd, vd, row_ptr, col_idx, work_order=order, **kw)
     o_iv = cba.sparse_attn_fwd_intervals(qd, kd, vd, iv_ptr, ivs, work_order=order, **kw)
     energy, lse, od = cba.calib_block_energy(qd, kd, vd, block=block, n_prefix=n_prefix, grid=grid)
+    e1, l1, o1 = cba.calib_block_energy_ws(qd, kd, vd, block=block, n_prefix=n_prefix, grid=grid)
     taus = rng.uniform(0.5, 0.99, heads)
     sel, votes = cba.select_blocks_by_energy_heads(energy, taus, 0.5, True, n_prefix // block, return_votes=True)
     torch.cuda.synchronize()
@@ -74,6 +77,8 @@ def test_random_shape(seed):
     packed = (first.astype(np.uint32) | (count.astype(np.uint32) << np.uint32(16))).view(np.int32)
     np.testing.assert_array_equal(ivs.cpu().numpy()[:ip[-1]], packed)
     assert torch.equal(o, o_iv)
+    # one-pass energies: O and LSE are the dense pass's bits
+    assert torch.equal(o1, od) and torch.equal(l1, lse)
     # selection on the GPU's own energies: bit-exact
     ref_sel, ref_votes = oracle.select_blocks(to_host(energy), taus, 0.5, True, n_prefix // block)
     np.testing.assert_array_equal(sel.cpu().numpy(), ref_sel)
@@ -88,6 +93,7 @@ def test_random_shape(seed):
             assert_close_out(to_host(od)[b, h], refd, dtype, f"case {seed} energy-pass O b{b} h{h}")
             ref_e = oracle.block_energy(q[b, h], k[b, h], block)
             assert np.abs(to_host(energy)[b, h] - ref_e).max() <= etol
+            assert np.abs(to_host(e1)[b, h] - ref_e).max() <= etol
     # repetition detection where the grid has follower rows
     if stride >= 2 and grid[1] >= 2:
         hs, tc = cba.spatial_rep_similarity(qd, kd, lse, stride, n_prefix=n_prefix, grid=grid)
