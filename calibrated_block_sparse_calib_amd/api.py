@@ -74,6 +74,12 @@ def _check_out(t: Optional[torch.Tensor], shape, dtype, name: str):
         raise CalibAttnError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
 
 
+def _out_like(q: torch.Tensor) -> torch.Tensor:
+    """A new output tensor with exactly q's shape and strides (the library writes O
+    with the strides it reads Q with)."""
+    return torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+
+
 def _rep_array(rep_heads, heads):
     if rep_heads is None:
         return None, None
@@ -104,7 +110,7 @@ def calib_block_energy(q, k, v=None, *, block: int, n_prefix: int = 0, grid=None
     if energy is None:
         energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
     if v is not None and o is None:
-        o = torch.empty_like(q)
+        o = _out_like(q)
     _check(_lib.load().calib_block_energy(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                           _ptr(lse), _ptr(energy), _stream()), "calib_block_energy")
     return energy, lse, o
@@ -158,7 +164,7 @@ def calib_block_energy_ws(q, k, v=None, *, block: int, n_prefix: int = 0, grid=N
     if energy is None:
         energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
     if v is not None and o is None:
-        o = torch.empty_like(q)
+        o = _out_like(q)
     need = energy_workspace_bytes(q, block)
     if workspace is None:
         workspace = torch.empty(need if q.dtype == torch.bfloat16 else 16, dtype=torch.uint8, device=q.device)
@@ -218,13 +224,14 @@ def select_blocks_by_energy_heads(energy: torch.Tensor, tau_heads, rho: float = 
     return (mask, votes) if return_votes else mask
 
 
-def build_block_csr(mask: torch.Tensor, with_order: bool = True, exact: bool = False,
-                    ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+def build_block_csr(mask: torch.Tensor, with_order: bool = True, exact: bool = False, count_only: bool = False,
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     """mask uint8 [..., nkb] (rows = all leading dims) -> (row_ptr, col_idx, work_order).
 
     exact=False: one call with capacity rows * nkb (no host synchronisation); the
     first row_ptr[-1] entries of col_idx are the skip list.  exact=True: a count
-    pass, a host read of nnz, then the fill into a tensor of exactly nnz entries."""
+    pass, a host read of nnz, then the fill into a tensor of exactly nnz entries.
+    count_only=True: the count pass alone, returning (row_ptr, None, None)."""
     _require_gpu(mask)
     if mask.dtype != torch.uint8 or not mask.is_contiguous():
         raise CalibAttnError("mask must be contiguous uint8")
@@ -232,6 +239,10 @@ def build_block_csr(mask: torch.Tensor, with_order: bool = True, exact: bool = F
     rows = mask.numel() // nkb
     lib = _lib.load()
     row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=mask.device)
+    if count_only:
+        _check(lib.build_block_csr(_ptr(mask), rows, nkb, _ptr(row_ptr), None, 0, None, _stream()),
+               "build_block_csr(count)")
+        return row_ptr, None, None
     order = torch.empty(rows, dtype=torch.int32, device=mask.device) if with_order else None
     if exact:
         _check(lib.build_block_csr(_ptr(mask), rows, nkb, _ptr(row_ptr), None, 0, None, _stream()),
@@ -296,7 +307,7 @@ def sparse_attn_fwd_intervals(q, k, v, iv_ptr, ivs, *, block: int, work_order=No
     """sparse_attn_fwd with the skip list as block intervals (build_block_intervals)."""
     _require_gpu(q, k, v, iv_ptr, ivs, work_order, o, lse)
     if o is None:
-        o = torch.empty_like(q)
+        o = _out_like(q)
     _same_layout(q, k, v, o)
     desc = make_desc(q, block, n_prefix, grid, scale)
     b, h, n, _ = q.shape
@@ -329,7 +340,7 @@ def sparse_attn_fwd(q, k, v, row_ptr, col_idx, *, block: int, work_order=None, r
     """Block-sparse attention over the kept blocks in (row_ptr, col_idx)."""
     _require_gpu(q, k, v, row_ptr, col_idx, work_order, o, lse)
     if o is None:
-        o = torch.empty_like(q)
+        o = _out_like(q)
     _same_layout(q, k, v, o)
     desc = make_desc(q, block, n_prefix, grid, scale)
     b, h, n, _ = q.shape
@@ -371,7 +382,7 @@ def dense_attn_fwd(q, k, v, *, block: int = 128, scale: float = 0.0, o: Optional
     """Dense attention over every key (the baseline)."""
     _require_gpu(q, k, v, o, lse)
     if o is None:
-        o = torch.empty_like(q)
+        o = _out_like(q)
     _same_layout(q, k, v, o)
     desc = make_desc(q, block, 0, None, scale)
     b, h, n, _ = q.shape

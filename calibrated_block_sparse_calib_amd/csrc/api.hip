@@ -145,7 +145,7 @@ CBA_API cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* 
   const int64_t need = (int64_t)desc->batch * desc->heads * p.nb * p.nb * desc->block * (int64_t)sizeof(float);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return CBA_EINVAL;
   if (workspace_bytes < need) return CBA_ECAPACITY;
-  return from_hip(cba::launch_energy1_bf16(p, desc->head_dim, desc->block, static_cast<float*>(workspace), s));
+  return from_hip(cba::launch_energy1_bf16(p, desc->head_dim, desc->block, static_cast<float*>(workspace), -1, s));
 }
 
 CBA_API cba_status select_blocks_by_energy(const float* energy, int32_t n_draws, int32_t heads, int32_t nb,

@@ -136,13 +136,14 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
   constexpr int LPW = C::KT / (64 / (D / 8)) / C::NW;
   int voff[LPW];
   if (BUF) tile_lane_offsets<D, C::KT, C::NW>((int)(p.sn * 2), voff);
-  const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
+  const TileSrc ksrc = tile_src<D>(kg, p.n, p.sn), vsrc = tile_src<D>(vg, p.n, p.sn);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // A step with no key block (k0 < 0, uniform) stages nothing: its compute is skipped.
   auto load = [&](int k0, bfraw* kdst, bfraw* vdst) {
+    if (k0 < 0) return;
     if (BUF) {
-      const int so = k0 * (int)(p.sn * 2);
-      load_tile_buf(kg, nrec, voff, LPW, so, kdst + wv * LPW * 512);
-      if (PV) load_tile_buf(vg, nrec, voff, LPW, so, vdst + wv * LPW * 512);
+      load_tile_buf(ksrc, k0, voff, LPW, kdst + wv * LPW * 512);
+      if (PV) load_tile_buf(vsrc, k0, voff, LPW, vdst + wv * LPW * 512);
     } else {
       load_tile<D, C::KT, C::NW>(kg, p.sn, p.n, k0, kdst);
       if (PV) load_tile<D, C::KT, C::NW>(vg, p.sn, p.n, k0, vdst);
@@ -361,10 +362,11 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy_bf16_kernel(A
   constexpr int LPW = C::KT / (64 / (D / 8)) / NW;
   int voff[LPW];
   if (BUF) tile_lane_offsets<D, C::KT, NW>((int)(p.sn * 2), voff);
-  const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
+  const TileSrc ksrc = tile_src<D>(kg, p.n, p.sn);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto load = [&](int k0, bfraw* kdst) {
-    if (BUF) load_tile_buf(kg, nrec, voff, LPW, k0 * (int)(p.sn * 2), kdst + wv * LPW * 512);
+    if (k0 < 0) return;
+    if (BUF) load_tile_buf(ksrc, k0, voff, LPW, kdst + wv * LPW * 512);
     else load_tile<D, C::KT, NW>(kg, p.sn, p.n, k0, kdst);
   };
   float esum = 0.f;

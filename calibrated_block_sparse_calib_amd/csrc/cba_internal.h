@@ -87,9 +87,13 @@ inline int64_t rep_grid(int batch, int heads, int gf, int gh, int gw, int stride
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block, bool with_pv, hipStream_t stream);
 hipError_t launch_energy_bf16(const AttnParams& p, int head_dim, int block, hipStream_t stream);
 // One-pass energies with the per-(row, key block) log-sums in ws [batch, heads, nb, nb, block]
-// (O too when p.v is set; the _k variant is the case without V).
-hipError_t launch_energy1_bf16(const AttnParams& p, int head_dim, int block, float* ws, hipStream_t stream);
-hipError_t launch_energy1_k_bf16(const AttnParams& p, int head_dim, int block, float* ws, hipStream_t stream);
+// (O too when p.v is set; the _k variant is the case without V).  ws_bytes < 0: ws
+// holds all of it; otherwise ws holds ws_bytes and the work goes in several
+// launches (hipErrorInvalidValue if one workgroup's rows do not fit).
+hipError_t launch_energy1_bf16(const AttnParams& p, int head_dim, int block, float* ws, int64_t ws_bytes,
+                               hipStream_t stream);
+hipError_t launch_energy1_k_bf16(const AttnParams& p, int head_dim, int block, float* ws, int64_t ws_bytes,
+                                 hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, int block, bool with_pv, hipStream_t stream);
 hipError_t launch_energy_f32(const AttnParams& p, int head_dim, int block, hipStream_t stream);
 hipError_t launch_select(const float* energy, int n_draws, int heads, int nb, const TauTable& taus, double rho,

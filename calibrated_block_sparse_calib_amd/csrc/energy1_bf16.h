@@ -12,6 +12,8 @@
 // instruction-scheduling strategies (build.py).
 #pragma once
 
+#include <algorithm>
+
 #include "cba_internal.h"
 #include "mfma_util.h"
 
@@ -33,8 +35,14 @@ using namespace dev;
 // PV: the pass also multiplies by V and writes O, step for step as attn_item's
 // dense pass (same weights, same order), so O and the LSE are those of
 // dense_attn_fwd bit for bit.
+// Items run (batch item, head)-major: item = (b * heads + h) * nqg + query-block
+// group, so a contiguous range of items owns a contiguous range of workspace rows
+// (row = (b * heads + h) * nb + qb).  A launch covers items item0 + blockIdx.x and
+// holds the workspace rows from ws_row0 on at ws, so a workspace smaller than the
+// whole problem can serve it in several launches.
 template <int D, int B, int QPB, bool PV, bool BUF>
-__global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(AttnParams p, float* ws) {
+__global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(AttnParams p, float* ws,
+                                                                                int64_t item0, int64_t ws_row0) {
   using C = Cfg<D, B>;
   constexpr int NW = QPB * C::NW;  // waves per workgroup, 32 rows each
   __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
@@ -42,10 +50,11 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
   __shared__ float lse2_s[QPB * B];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-  const int item = blockIdx.x;
-  const int it = item / p.batch, b = item - it * p.batch;
   const int nqg = (p.nb + QPB - 1) / QPB;
-  const int h = it / nqg, qb0 = (it - h * nqg) * QPB;
+  const int64_t item = item0 + blockIdx.x;
+  const int bhi = (int)(item / nqg), qgrp = (int)(item - (int64_t)bhi * nqg);
+  const int b = bhi / p.heads, h = bhi - b * p.heads;
+  const int qb0 = qgrp * QPB;
   const int q0 = qb0 * B;
   const int M = min(QPB * B, p.n - q0);
 
@@ -57,9 +66,9 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
   const bool wave_active = wave * 32 < M;
   const bool q_valid = qi < M;
   const int qtok = q0 + qi;
-  const int64_t bh = (int64_t)b * p.heads + h;
+  const int64_t bh = bhi;
   // [kb][B] slice of this row's query block (only dereferenced for valid rows)
-  float* wrow = ws + ((bh * p.nb + qb0 + qi / B) * (int64_t)p.nb) * B + qi % B;
+  float* wrow = ws + ((bh * p.nb + qb0 + qi / B - ws_row0) * (int64_t)p.nb) * B + qi % B;
 
   bf16x8 qf[C::KS];
 #pragma unroll
@@ -76,13 +85,13 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
   constexpr int LPW = C::KT / (64 / (D / 8)) / NW;
   int voff[LPW];
   if (BUF) tile_lane_offsets<D, C::KT, NW>((int)(p.sn * 2), voff);
-  const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
+  const TileSrc ksrc = tile_src<D>(kg, p.n, p.sn), vsrc = tile_src<D>(vg, p.n, p.sn);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto load = [&](int k0, bfraw* kdst, bfraw* vdst) {
+    if (k0 < 0) return;
     if (BUF) {
-      const int so = k0 * (int)(p.sn * 2);
-      load_tile_buf(kg, nrec, voff, LPW, so, kdst + wv * LPW * 512);
-      if (PV) load_tile_buf(vg, nrec, voff, LPW, so, vdst + wv * LPW * 512);
+      load_tile_buf(ksrc, k0, voff, LPW, kdst + wv * LPW * 512);
+      if (PV) load_tile_buf(vsrc, k0, voff, LPW, vdst + wv * LPW * 512);
     } else {
       load_tile<D, C::KT, NW>(kg, p.sn, p.n, k0, kdst);
       if (PV) load_tile<D, C::KT, NW>(vg, p.sn, p.n, k0, vdst);
@@ -243,7 +252,7 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(
     const int j = idx / p.nb, kb = idx - j * p.nb;
     const int Mj = M - j * B;  // valid rows of query block qb0 + j
     if (Mj <= 0) break;        // uniform over the wave; later pairs have larger j
-    const float* L = ws + ((bh * p.nb + qb0 + j) * (int64_t)p.nb + kb) * B;
+    const float* L = ws + ((bh * p.nb + qb0 + j - ws_row0) * (int64_t)p.nb + kb) * B;
     float e = 0.f;
 #pragma unroll
     for (int r = lane; r < B; r += 64)
@@ -260,17 +269,48 @@ constexpr int energy1_qpb() {
 }
 
 // Launch with Q query blocks per workgroup (with V, Q = 1 as in the dense pass).
+// ws_bytes < 0: ws holds the whole problem's workspace, one launch.  Otherwise ws
+// holds ws_bytes and the items go in consecutive launches, each over the longest
+// run of items whose workspace rows fit.
 template <int D, int B, int Q, bool PV>
-hipError_t launch_energy1_q(const AttnParams& p, float* ws, hipStream_t stream) {
+hipError_t launch_energy1_q(const AttnParams& p, float* ws, int64_t ws_bytes, hipStream_t stream) {
   using C = Cfg<D, B>;
   const int64_t nqg = (p.nb + Q - 1) / Q;
-  const dim3 grid((unsigned)((int64_t)p.heads * nqg * p.batch)), block(Q * C::NT);
+  const int64_t n_items = (int64_t)p.heads * p.batch * nqg;
+  const dim3 block(Q * C::NT);
   const bool buf = (int64_t)(p.n + C::KT) * p.sn * 2 < ((int64_t)1 << 31);
   auto kern = buf ? energy1_bf16_kernel<D, B, Q, PV, true> : energy1_bf16_kernel<D, B, Q, PV, false>;
   AttnParams arg = p;
   float* w = ws;
-  void* args[] = {&arg, &w};
-  return hipLaunchKernel((const void*)kern, grid, block, args, 0, stream);
+  const int64_t row_bytes = (int64_t)p.nb * B * (int64_t)sizeof(float);
+  // First workspace row of item i and one past its last.
+  auto row_lo = [&](int64_t i) { return (i / nqg) * p.nb + (i % nqg) * Q; };
+  auto row_hi = [&](int64_t i) { return (i / nqg) * p.nb + std::min<int64_t>((i % nqg) * Q + Q, p.nb); };
+  const int64_t max_rows = ws_bytes < 0 ? row_hi(n_items - 1) : ws_bytes / row_bytes;
+  for (int64_t i0 = 0; i0 < n_items;) {
+    int64_t i1 = n_items;
+    int64_t r0 = row_lo(i0);
+    if (ws_bytes >= 0) {
+      // largest i1 with row_hi(i1 - 1) - r0 <= max_rows (row_hi grows with i)
+      int64_t lo = i0, hi = n_items;  // row_hi(lo) - r0 <= max_rows is checked below
+      if (row_hi(i0) - r0 > max_rows) return hipErrorInvalidValue;
+      while (hi - lo > 1) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (row_hi(mid) - r0 <= max_rows) lo = mid;
+        else hi = mid;
+      }
+      i1 = lo + 1;
+    } else {
+      r0 = 0;
+    }
+    const dim3 grid((unsigned)(i1 - i0));
+    int64_t it0 = i0, wr0 = r0;
+    void* args[] = {&arg, &w, &it0, &wr0};
+    hipError_t e = hipLaunchKernel((const void*)kern, grid, block, args, 0, stream);
+    if (e != hipSuccess) return e;
+    i0 = i1;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

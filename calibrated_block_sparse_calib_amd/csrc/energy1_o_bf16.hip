@@ -4,10 +4,11 @@
 
 namespace cba {
 
-hipError_t launch_energy1_bf16(const AttnParams& p, int head_dim, int block, float* ws, hipStream_t stream) {
-  if (!p.v) return launch_energy1_k_bf16(p, head_dim, block, ws, stream);
+hipError_t launch_energy1_bf16(const AttnParams& p, int head_dim, int block, float* ws, int64_t ws_bytes,
+                               hipStream_t stream) {
+  if (!p.v) return launch_energy1_k_bf16(p, head_dim, block, ws, ws_bytes, stream);
 #define CBA_CASE(D, B) \
-  if (head_dim == D && block == B) return launch_energy1_q<D, B, 1, true>(p, ws, stream);
+  if (head_dim == D && block == B) return launch_energy1_q<D, B, 1, true>(p, ws, ws_bytes, stream);
   CBA_CASE(64, 32) CBA_CASE(64, 64) CBA_CASE(64, 128)
   CBA_CASE(128, 32) CBA_CASE(128, 64) CBA_CASE(128, 128)
 #undef CBA_CASE

@@ -98,9 +98,9 @@ __device__ inline int tile_off(int r, int d) {
 // lane's 16 bytes land at the instruction's LDS base + 16 * lane, no registers).
 // NW waves split the tile; wave load j of a wave covers 1 KB = 64 / (D / 8) rows.
 // Physical chunk i % (D/8) of row rr holds logical chunk (i % (D/8)) ^ swz(rr).
-// Rows past the end of the sequence reread the last row and an invalid step
-// (k0 < 0) reads the first rows: such keys are masked or skipped, so their
-// values only need to be finite.
+// Rows past the end of the sequence reread the last row, a valid input row: such
+// keys are masked out of the scores and get zero weight.  Callers pass
+// 0 <= k0 < n.
 template <int D, int KT, int NW>
 __device__ inline void load_tile(const bfraw* src, int64_t sn, int n, int k0, bfraw* tile) {
   constexpr int CPR = D / 8, RPI = 64 / CPR, LPW = KT / RPI / NW;
@@ -120,11 +120,12 @@ __device__ inline void load_tile(const bfraw* src, int64_t sn, int n, int k0, bf
 
 // Buffer-load variant of load_tile, for tiles addressed with 32-bit byte offsets:
 // the lane offsets inside a tile are fixed (tile_lane_offsets, once per kernel)
-// and the tile's first key enters as one scalar offset, so a tile load costs no
-// vector instructions.  The buffer covers the nrec bytes at base; rows past it
-// read as zeros.  The resource is built here, in device-only code, because the
-// host compilation also sees kernels and their lambdas and has no
-// buffer-resource type.
+// and the tile's first key only moves the buffer's base, a scalar computation, so
+// a tile load costs no vector instructions.  The buffer of a tile starts at its
+// first key row and ends at the last byte of the sequence: the range check
+// applies to the lane offsets, so rows past the end read as zeros.  The resource
+// is built here, in device-only code, because the host compilation also sees
+// kernels and their lambdas and has no buffer-resource type.
 template <int D, int KT, int NW>
 __device__ inline void tile_lane_offsets(int row_bytes, int* voff) {
   constexpr int CPR = D / 8, RPI = 64 / CPR, LPW = KT / RPI / NW;
@@ -136,13 +137,30 @@ __device__ inline void tile_lane_offsets(int row_bytes, int* voff) {
   }
 }
 
-__device__ __forceinline__ void load_tile_buf(const void* base, int nrec, const int* voff, int lpw, int so,
-                                              bfraw* dst) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec,
-                                                                      0x00020000);
+// One head's rows of K or V as seen by the buffer loads: base, bytes per row and
+// bytes from the base to the end of the last row's D values.
+struct TileSrc {
+  const bfraw* base;
+  int row_bytes;
+  int end_bytes;
+};
+
+template <int D>
+__device__ inline TileSrc tile_src(const bfraw* base, int n, int64_t sn) {
+  return TileSrc{base, (int)(sn * 2), (int)(((int64_t)(n - 1) * sn + D) * 2)};
+}
+
+// Stages the tile whose first key is k0 (0 <= k0 < n, uniform over the
+// workgroup); lpw loads per wave, each of 64 lanes x 16 bytes, at dst.
+__device__ __forceinline__ void load_tile_buf(const TileSrc& t, int k0, const int* voff, int lpw, bfraw* dst) {
+  const int kk = __builtin_amdgcn_readfirstlane(k0);
+  const char* b = reinterpret_cast<const char*>(t.base) + (int64_t)kk * t.row_bytes;
+  const int nrec = t.end_bytes - kk * t.row_bytes;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, nrec, 0x00020000);
 #pragma unroll
   for (int j = 0; j < lpw; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + j * 512), 16, voff[j], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + j * 512), 16, voff[j], 0, 0, 0);
 }
 
 // Token rows of query block qb that this workgroup computes.  Normal heads: all

@@ -72,10 +72,10 @@ __global__ __launch_bounds__(kRepGroups * NWV * 64, 2) void rep_sim_bf16_kernel(
   constexpr int LPW = kKT / (64 / (D / 8)) / NW;
   int voff[LPW];
   if (BUF) tile_lane_offsets<D, kKT, NW>((int)(p.sn * 2), voff);
-  const int nrec = (int)(((int64_t)(p.n - 1) * p.sn + D) * 2);
+  const TileSrc ksrc = tile_src<D>(kg, p.n, p.sn);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto load = [&](int k0, bfraw* kdst) __attribute__((always_inline)) {
-    if (BUF) load_tile_buf(kg, nrec, voff, LPW, k0 * (int)(p.sn * 2), kdst + wv * LPW * 512);
+    if (BUF) load_tile_buf(ksrc, k0, voff, LPW, kdst + wv * LPW * 512);
     else load_tile<D, kKT, NW>(kg, p.sn, p.n, k0, kdst);
   };
 

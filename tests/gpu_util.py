@@ -9,6 +9,34 @@ BF16_MAX, BF16_MEAN = 1e-2, 1e-3  # bf16 inputs, fp32 accumulation
 F32_MAX = 1e-5  # fp32 path
 
 
+def bf16_half_ulp(x):
+    """Half the spacing of bf16 numbers at |x| (0 at x = 0): the most that storing a
+    value of that magnitude in bf16 moves it.  It reaches 7.8e-3 for |x| in [2, 4)
+    and 1.6e-2 for |x| in [4, 8)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(a)  # a = m * 2**e with m in [0.5, 1): the bf16 spacing there is 2**(e - 8)
+    return np.where(a > 0, np.ldexp(1.0, e - 9), 0.0)
+
+
+def bf16_excess(got, ref):
+    """|got - ref| beyond the bf16 rounding of the stored output got: the error the
+    fp32 computation made.  The max bar applies to this; the mean bar to |got - ref|."""
+    got = np.asarray(got, dtype=np.float64)
+    return np.abs(got - ref) - bf16_half_ulp(got)
+
+
+def check_bf16_outputs(got, ref, what=""):
+    """Max and mean bars of bf16 outputs: max of bf16_excess <= 1e-2, mean |got - ref|
+    <= 1e-3.  Returns (max |got - ref|, max excess, mean)."""
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    exc = bf16_excess(got, ref)
+    mx, mx_exc, mean = float(err.max()), float(exc.max()), float(err.mean())
+    assert mx_exc <= BF16_MAX and mean <= BF16_MEAN, (
+        f"{what}: max {mx:.3e} (beyond bf16 rounding {mx_exc:.3e}) mean {mean:.3e}")
+    return mx, mx_exc, mean
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -33,7 +61,9 @@ def assert_close_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, ro
     at = np.unravel_index(int(np.argmax(err)), err.shape)
     info = f"{what}: max {mx:.3e} at {at} (ref {float(ref[at]):.4f}, got {float(got[at]):.4f}) mean {mean:.3e}"
     if dtype == "bf16":
-        assert mx <= BF16_MAX and mean <= BF16_MEAN, info
+        exc = float(bf16_excess(got, ref).max())
+        info += f", beyond bf16 rounding {exc:.3e}"
+        assert exc <= BF16_MAX and mean <= BF16_MEAN, info
     else:
         assert mx <= F32_MAX, info
     log("  ok " + info)

@@ -2,7 +2,8 @@
 oracle: energies |dE| <= 1e-4 * block (bf16), LSE within 1e-3, repeated calls
 bit-identical, and the workspace size enforced.  With V, O and the LSE are
 bit-identical to calib_block_energy's dense pass and the energies to the one-pass
-result without V; O is also checked against the oracle (bf16 max 1e-2, mean 1e-3)."""
+result without V; O is also checked against the oracle (bf16 max 1e-2 beyond the
+output's bf16 rounding, mean 1e-3)."""
 import ctypes
 
 import numpy as np
@@ -37,7 +38,7 @@ def test_onepass_energy_matches_oracle(d, block, grid, n_prefix):
     draws = [make_qkv(cfg, draw=i) for i in range(2)]
     q = np.stack([x[0] for x in draws])
     k = np.stack([x[1] for x in draws])
-    v = np.stack([x[2] for x in draws]) * 0.5  # halved (exact): |o| stays below 4, where bf16 spacing reaches the bar
+    v = np.stack([x[2] for x in draws])
     qd, kd, vd = (torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda() for x in (q, k, v))
     e1, l1, _ = cba.calib_block_energy_ws(qd, kd, block=block)
     e1b, l1b, _ = cba.calib_block_energy_ws(qd, kd, block=block)

@@ -1,7 +1,8 @@
 """Seeded random shapes through every call, against the fp64 oracle: head_dim,
 block, token grid, text prefix, anchor stride, mask density, dtype and batch drawn
 from a fixed seed per case, so that corners no hand-picked case covers get
-exercised.  Bars as elsewhere: bf16 max 1e-2 / mean 1e-3, fp32 max 1e-5, energies
+exercised.  Bars as elsewhere: bf16 max 1e-2 beyond the output's bf16 rounding /
+mean 1e-3, fp32 max 1e-5, energies
 1e-4 * block (1e-5 * block in fp32), repetition cosines 1e-4 (1e-5 in fp32),
 integer results bit-exact."""
 import os
@@ -48,7 +49,7 @@ def test_random_shape(seed):
     x = [rng.standard_normal((batch, heads, n, d)).astype(np.float32) for _ in range(3)]
     if dtype == "bf16":
         x = [torch.from_numpy(a).to(torch.bfloat16).float().numpy() for a in x]
-    q, k, v = x[0], x[1], x[2] * 0.5  # V halved (exact): |o| stays below 4, where bf16 spacing reaches the bar
+    q, k, v = x
     dev = lambda a: (torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16) if dtype == "bf16"
                      else torch.from_numpy(np.ascontiguousarray(a))).cuda()
     qd, kd, vd = dev(q), dev(k), dev(v)

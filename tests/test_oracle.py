@@ -53,6 +53,29 @@ def test_dense_closed_forms():
     np.testing.assert_allclose(o, np.repeat(c, n, 0), atol=1e-13)
 
 
+def test_dense_lse_matches_scipy_logsumexp():
+    """The LSE against scipy's logsumexp of the scaled logits (a second library)."""
+    from scipy.special import logsumexp
+
+    for n, d, seed in ((9, 4, 30), (80, 16, 31)):
+        q, k, v = _rand((n, d), seed), 3.0 * _rand((n, d), seed + 1), _rand((n, d), seed + 2)
+        _, lse = oracle.dense_attention(q, k, v)
+        np.testing.assert_allclose(lse, logsumexp(q @ k.T / math.sqrt(d), axis=1), rtol=0, atol=1e-12)
+
+
+def test_dense_shift_invariance():
+    """Adding one vector u to every key adds scale * q_i . u to every logit of row i:
+    the softmax of each row is unchanged (so O is), and the LSE moves by exactly that
+    per-row constant.  A softmax over the wrong axis, or a dropped max shift, fails."""
+    n, d = 30, 8
+    q, k, v = _rand((n, d), 40), _rand((n, d), 41), _rand((n, d), 42)
+    u = 4.0 * _rand((1, d), 43)
+    o0, lse0 = oracle.dense_attention(q, k, v)
+    o1, lse1 = oracle.dense_attention(q, k + u, v)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse1 - lse0, (q @ u[0]) / math.sqrt(d), rtol=0, atol=1e-11)
+
+
 def test_dense_explicit_scale():
     q, k, v = _rand((20, 8), 8), _rand((20, 8), 9), _rand((20, 8), 10)
     o, _ = oracle.dense_attention(q, k, v, scale=0.37)
@@ -303,6 +326,30 @@ def test_sparse_full_mask_is_dense_and_diagonal_is_blockwise():
     for b in range(nb):
         sl = slice(b * block, (b + 1) * block)
         np.testing.assert_allclose(o[sl], _sdpa(q[sl], k[sl], v[sl], 1 / math.sqrt(d)), atol=1e-12)
+
+
+def test_sparse_masked_values_change_nothing():
+    """For the rows of one query block, the V and K rows of key blocks outside its
+    mask take no part: perturbing them (even by huge values) leaves those rows'
+    outputs and LSE bit-identical.  Masking by a zero weight after the softmax, or
+    over the wrong block row, fails."""
+    n, d, block = 96, 8, 16
+    nb = n // block
+    q, k, v = _rand((n, d), 50), _rand((n, d), 51), _rand((n, d), 52)
+    rng = np.random.default_rng(53)
+    mask = rng.random((nb, nb)) < 0.4
+    np.fill_diagonal(mask, True)
+    for qb in range(nb):
+        rows = np.zeros(n, dtype=bool)
+        rows[qb * block:(qb + 1) * block] = True
+        o0, lse0 = oracle.sparse_attention(q, k, v, mask, block, rows=rows)
+        k2, v2 = k.copy(), v.copy()
+        for kb in np.nonzero(~mask[qb])[0]:
+            k2[kb * block:(kb + 1) * block] += 1e3 * _rand((block, d), 54 + kb)
+            v2[kb * block:(kb + 1) * block] = 1e6 * _rand((block, d), 70 + kb)
+        o1, lse1 = oracle.sparse_attention(q, k2, v2, mask, block, rows=rows)
+        np.testing.assert_array_equal(o1[rows], o0[rows])
+        np.testing.assert_array_equal(lse1[rows], lse0[rows])
 
 
 def test_sparse_empty_rows_and_row_subset():
