@@ -9,6 +9,7 @@ from .api import (
     build_block_csr,
     build_block_intervals,
     calib_block_energy,
+    calib_block_energy_noalloc,
     calib_block_energy_ws,
     dense_attn_fwd,
     energy_workspace_bytes,
@@ -34,6 +35,7 @@ __all__ = [
     "build_block_csr",
     "build_block_intervals",
     "calib_block_energy",
+    "calib_block_energy_noalloc",
     "calib_block_energy_ws",
     "dense_attn_fwd",
     "energy_workspace_bytes",

@@ -45,6 +45,7 @@ SIGNATURES = {
     "order_heavy_rows_first": (c_i32, [c_p, c_i32, c_i32, c_f64, c_p, c_p]),
     "block_energy_from_lse": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p]),
     "calib_block_energy_ws": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_p]),
+    "calib_block_energy_noalloc": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "select_blocks_by_energy_heads": (c_i32, [c_p, c_i32, c_i32, c_i32, c_p, c_f64, c_i32, c_i32, c_p, c_p, c_p]),
     "sparse_attn_fwd_intervals": (c_i32, [_PD, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p, c_i32, c_i32, c_p, c_p,
                                           c_p]),

@@ -177,6 +177,36 @@ def calib_block_energy_ws(q, k, v=None, *, block: int, n_prefix: int = 0, grid=N
     return energy, lse, o
 
 
+NOALLOC_MAX_BYTES = 256 << 20  # the library's fixed per-GPU array behind calib_block_energy_noalloc
+
+
+def calib_block_energy_noalloc(q, k, v=None, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,
+                               lse: Optional[torch.Tensor] = None, energy: Optional[torch.Tensor] = None,
+                               o: Optional[torch.Tensor] = None):
+    """calib_block_energy_ws with no workspace: the library keeps the one-pass
+    log-sums in a fixed device array of its own (NOALLOC_MAX_BYTES per GPU) and
+    allocates nothing.  Outputs not given are allocated here, by torch, before the
+    call.  Calls that overlap on one GPU share that array and must not run
+    concurrently.  Returns (energy, lse, o); o is None without v."""
+    _require_gpu(q, k, v, lse, energy, o)
+    _same_layout(q, k, v, o)
+    desc = make_desc(q, block, n_prefix, grid, scale)
+    b, h, n, _ = q.shape
+    nb = n_blocks(n, block)
+    _check_out(lse, (b, h, n), torch.float32, "lse")
+    _check_out(energy, (b, h, nb, nb), torch.float32, "energy")
+    if lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if energy is None:
+        energy = torch.empty((b, h, nb, nb), dtype=torch.float32, device=q.device)
+    if v is not None and o is None:
+        o = _out_like(q)
+    _check(_lib.load().calib_block_energy_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                                  _ptr(lse), _ptr(energy), _stream()),
+           "calib_block_energy_noalloc")
+    return energy, lse, o
+
+
 def block_energy_from_lse(q, k, lse, *, block: int, n_prefix: int = 0, grid=None, scale: float = 0.0,
                           energy: Optional[torch.Tensor] = None):
     """Energy sweep alone from a given (possibly cached) LSE fp32 [batch, heads, seq_len].

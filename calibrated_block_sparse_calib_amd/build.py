@@ -18,7 +18,7 @@ LIB_NAME = "libcalibattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [
     "api.hip", "attn_bf16.hip", "energy1_bf16.hip", "energy1_o_bf16.hip", "attn_f32.hip", "select_csr.hip",
-    "repetition.hip",
+    "repetition.hip", "noalloc.hip",
 ]
 ARCH = "gfx950"
 

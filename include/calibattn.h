@@ -103,6 +103,22 @@ cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* q, const
                                  float* lse, float* energy, void* workspace, int64_t workspace_bytes,
                                  cba_stream_t stream);
 
+/* calib_block_energy_ws for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument.  The log-sums go to a fixed 256 MiB device array of the
+ * library, one per GPU, held from the first call on that GPU until the process
+ * ends; the call allocates nothing.  When the problem's workspace
+ * (batch * heads * nb * nb * block floats) exceeds the array, the work runs in
+ * several consecutive launches over contiguous (batch item, head, query block)
+ * ranges; results are bit-identical to calib_block_energy_ws's.  CBA_ECAPACITY
+ * (nothing enqueued) only if one workgroup's rows alone exceed the array.
+ * Calls that overlap in time on one GPU (two streams or threads) share the array
+ * and race: the caller must serialise them.  The stream must belong to the
+ * current device (CBA_EINVAL otherwise).  Arguments, outputs and the fp32 case
+ * as calib_block_energy_ws. */
+cba_status calib_block_energy_noalloc(const cba_attn_desc* desc, const void* q, const void* k, const void* v,
+                                      void* o, float* lse, float* energy, cba_stream_t stream);
+
 /* Block energy sweep alone, from a given log-sum-exp ([AdaSpa] S2: the search pass
  * caches the LSE of its dense pass and later searches reuse that cache; zh S2.2A
  * for the tile energy).  energy[b, h, qb, kb] = sum over i in qb and j in kb of
