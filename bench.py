@@ -430,6 +430,9 @@ def main():
                          "(8 steps, searches at steps 0 and 4)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (calibrates HBM byte counters)")
+    ap.add_argument("--only", choices=["step", "dense"], default="step",
+                    help="dense: time only dense_attn_fwd (warmup + steps launches) and print its rate "
+                         "(profiling runs of the dense kernel)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -482,6 +485,21 @@ def main():
         assert st == 0, st
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    if args.only == "dense":
+        for _ in range(args.warmup):
+            cba.dense_attn_fwd(qd, kd, vd, block=B, o=od)
+        torch.cuda.synchronize()
+        marks = [(ev(), ev()) for _ in range(args.steps)]
+        for a, b_ in marks:
+            a.record(stream)
+            cba.dense_attn_fwd(qd, kd, vd, block=B, o=od)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        d_ms = statistics.mean(a.elapsed_time(b_) for a, b_ in marks)
+        print(json.dumps({"kernel": "dense_attn_fwd", "workload": cfg.name, "launches": args.steps, "ms": d_ms,
+                          "tflops": dense_flops / d_ms / 1e9,
+                          "frac_bf16_peak": dense_flops / d_ms / 1e9 / PEAK_BF16_TFLOPS}), flush=True)
+        return
     for _ in range(args.warmup):
         csr()
         sparse()

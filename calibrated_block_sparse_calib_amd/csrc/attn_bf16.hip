@@ -127,7 +127,6 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
   float m_used = -INFINITY;  // reference maximum, base-2 units
   float l_part = 0.f;        // this lane's share of the exact row sum (LSE)
   float r_part = 0.f;        // this lane's share of the rounded-weight sum (O)
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Even steps use buffers (k0s, v0s), odd steps (k1s, v1s).
   // BUF: tiles come by buffer loads with per-lane offsets fixed for the whole
@@ -164,98 +163,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
     if (s + 1 < nsteps) load(k0_next, kn, vn);
     k0_n1 = s + 2 < nsteps ? step_key0(s + 2) : -1;
     if (wave_active && k0_cur >= 0) {
-      const bool ragged = k0_cur + C::KT > p.n;
-      // S^T = K Q^T.  The K fragments are read PF fragments ahead of the MFMA that
-      // consumes them, so LDS latency overlaps the matrix-core work instead of
-      // stalling every MFMA.
       f32x16 sacc[C::ST];
-      constexpr int NF = C::ST * C::KS, PF = 3;
-      auto kfrag = [&](int f) {
-        return lds_read8(kt + tile_off<D>((f / C::KS) * 32 + (lane & 31), (f % C::KS) * 16 + g * 8));
-      };
-      bf16x8 kf[PF];
-#pragma unroll
-      for (int f = 0; f < PF; ++f) kf[f] = kfrag(f);
-#pragma unroll
-      for (int t = 0; t < C::ST; ++t) sacc[t] = f32x16{};
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const bf16x8 a = kf[f % PF];
-        if (f + PF < NF) kf[f % PF] = kfrag(f + PF);
-        sacc[f / C::KS] = mfma(a, qf[f % C::KS], sacc[f / C::KS]);
-      }
-      // Keys past the end of the sequence (ragged last block) take no part.  The
-      // empty asm keeps this rare block a real branch: the compiler would
-      // otherwise evaluate its compares and selects on every step.
-      if (ragged) {
-        asm volatile("" ::: "memory");
-        const int lim = p.n - k0_cur - g * 4;  // element (t, i) holds key k0 + t*32 + (i/4)*8 + g*4 + i%4
-#pragma unroll
-        for (int t = 0; t < C::ST; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (t * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[t][i] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < C::ST; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sacc[t][i]), sacc[t][i + 1]);  // v_max3 chain
-      mx = halves_max(mx);
-      const float mt = mx * p.c;
-      if (__ballot(mt > m_used + kLazyRescale)) {
-        asm volatile("" ::: "memory");  // rare: keep it a branch (see above)
-        const float m_new = fmaxf(m_used, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
-        l_part *= alpha;
-        r_part *= alpha;
-        if (PV) {
-#pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-        }
-        m_used = m_new;
-      }
+      qk_step<D, C::KT>(kt, qf, sacc);
+      if (k0_cur + C::KT > p.n) mask_ragged<C::ST>(sacc, p.n, k0_cur);
       bf16x8 pb[C::ST][2];
-      float ps = 0.f;
-#pragma unroll
-      for (int t = 0; t < C::ST; ++t)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][k2 * 8 + e], p.c, -m_used));
-            if (LSE || !PV) ps += x;
-            if (PV) pb[t][k2][e] = (__bf16)x;
-          }
-      l_part += ps;
-      if (PV) {
-#pragma unroll
-        for (int t = 0; t < C::ST; ++t)
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const bf16x2 pair = {pb[t][k2][e], pb[t][k2][e + 1]};
-              r_part = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, r_part, false);
-            }
-        const int G = lane >> 4, li = lane & 15;
-#pragma unroll
-        for (int t = 0; t < C::ST; ++t)
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const int krow = t * 32 + k2 * 16 + 4 * g + (li >> 2);
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) {
-              const int dcol = dt * 32 + (G & 1) * 16 + 4 * (li & 3);
-              const i16x4 lo = lds_read_tr(vt + tile_off<D>(krow, dcol));
-              const i16x4 hi = lds_read_tr(vt + tile_off<D>(krow + 8, dcol));
-              const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-              oacc[dt] = mfma(va, pb[t][k2], oacc[dt]);
-            }
-          }
-      }
+      softmax_step<C::ST, C::DT, PV, LSE>(sacc, p.c, m_used, l_part, r_part, oacc, pb);
+      if (PV) pv_step<D, C::KT>(vt, pb, oacc);
     }
     k0_cur = k0_next;
   };
@@ -382,26 +295,8 @@ __global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy_bf16_kernel(A
     }
     if (wave_active && k0_cur >= 0) {
       f32x16 sacc[C::ST];
-#pragma unroll
-      for (int t = 0; t < C::ST; ++t) {
-        sacc[t] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 a = lds_read8(kt + tile_off<D>(t * 32 + (lane & 31), ks * 16 + g * 8));
-          sacc[t] = mfma(a, qf[ks], sacc[t]);
-        }
-      }
-      if (k0_cur + C::KT > p.n) {
-        // Ragged last step: keys at or past the end add nothing.  Element (t, i)
-        // holds key k0 + t*32 + (i/4)*8 + g*4 + i%4.
-        asm volatile("" ::: "memory");  // rare: keep it a real branch
-        const int lim = p.n - k0_cur - g * 4;
-#pragma unroll
-        for (int t = 0; t < C::ST; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (t * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[t][i] = -INFINITY;
-      }
+      qk_step<D, C::KT>(kt, qf, sacc);
+      if (k0_cur + C::KT > p.n) mask_ragged<C::ST>(sacc, p.n, k0_cur);
 #pragma unroll
       for (int t = 0; t < C::ST; ++t)
 #pragma unroll

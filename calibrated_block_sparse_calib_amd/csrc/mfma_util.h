@@ -126,10 +126,11 @@ __device__ inline void load_tile(const bfraw* src, int64_t sn, int n, int k0, bf
 // applies to the lane offsets, so rows past the end read as zeros.  The resource
 // is built here, in device-only code, because the host compilation also sees
 // kernels and their lambdas and has no buffer-resource type.
+// wave: this wave's index among the NW waves that share the tile.
 template <int D, int KT, int NW>
-__device__ inline void tile_lane_offsets(int row_bytes, int* voff) {
+__device__ inline void tile_lane_offsets(int row_bytes, int* voff, int wave = threadIdx.x >> 6) {
   constexpr int CPR = D / 8, RPI = 64 / CPR, LPW = KT / RPI / NW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int rr = (wave * LPW + j) * RPI + lane / CPR;
@@ -196,9 +197,157 @@ __device__ int build_rowlist(const AttnParams& p, int q0, bool rep, int* rowlist
   return total;
 }
 
-// PV: compute O (otherwise only the log-sum-exp, for the energy sweep).
-// LSE: keep the exact fp32 row sum for the log-sum-exp output.
-// O is normalised by the sum of the same bf16-rounded weights that multiply V, so
-// rounding the weights perturbs a convex combination instead of scaling it.
+// ---------------------------------------------------------------------------
+// One key step of the attention-shaped kernels, shared by all of them so that
+// their arithmetic is the same instruction for instruction.  Per wave: 32 query
+// rows (lane l holds query l % 32 of the transposed score tile) against the KT
+// keys of the step staged in LDS.
+//
+// Scores, transposed: S^T = K Q^T with v_mfma_f32_32x32x16_bf16.  sacc[t] holds
+// keys t*32 .. t*32+31; element i of lane l is key t*32 + (i/4)*8 + (l/32)*4 + i%4
+// for query l % 32.  The K fragments are read PF fragments ahead of the MFMA that
+// consumes them, so LDS latency overlaps the matrix-core work.
+template <int D, int KT>
+__device__ __forceinline__ void qk_step(const bfraw* kt, const bf16x8* qf, f32x16* sacc) {
+  constexpr int KS = D / 16, ST = KT / 32, NF = ST * KS, PF = 3;
+  const int lane = threadIdx.x & 63, g = lane >> 5;
+  auto kfrag = [&](int f) {
+    return lds_read8(kt + tile_off<D>((f / KS) * 32 + (lane & 31), (f % KS) * 16 + g * 8));
+  };
+  bf16x8 kf[PF];
+#pragma unroll
+  for (int f = 0; f < PF; ++f) kf[f] = kfrag(f);
+#pragma unroll
+  for (int t = 0; t < ST; ++t) sacc[t] = f32x16{};
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const bf16x8 a = kf[f % PF];
+    if (f + PF < NF) kf[f % PF] = kfrag(f + PF);
+    sacc[f / KS] = mfma(a, qf[f % KS], sacc[f / KS]);
+  }
+}
+
+// Keys at or past the end of the sequence (a ragged last step starting at key k0)
+// take no part: their scores become -inf.  The empty asm keeps the caller's rare
+// branch a real branch (the compiler would otherwise evaluate the compares and
+// selects on every step).
+template <int ST>
+__device__ __forceinline__ void mask_ragged(f32x16* sacc, int n, int k0) {
+  asm volatile("" ::: "memory");
+  const int lim = n - k0 - (((threadIdx.x & 63) >> 5) * 4);
+#pragma unroll
+  for (int t = 0; t < ST; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (t * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[t][i] = -INFINITY;
+}
+
+// Maximum of N values as a tree of three-input maxima (v_max3_f32): depth about
+// log3 N instead of a chain of N / 2 dependent instructions.  Maxima are exact, so
+// the grouping does not change the result.
+template <int N>
+__device__ __forceinline__ float tree_max(const float* v) {
+  if constexpr (N == 1) {
+    return v[0];
+  } else if constexpr (N == 2) {
+    return fmaxf(v[0], v[1]);
+  } else {
+    constexpr int A = (N + 2) / 3, Bn = (N + 1) / 3;
+    return fmaxf(fmaxf(tree_max<A>(v), tree_max<Bn>(v + A)), tree_max<N - A - Bn>(v + A + Bn));
+  }
+}
+
+// Maximum over this lane's scores of the step and the other half-wave's (the same
+// query row).
+template <int ST>
+__device__ __forceinline__ float step_max(const f32x16* sacc) {
+  float v[ST * 16];
+#pragma unroll
+  for (int t = 0; t < ST; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[t * 16 + i] = sacc[t][i];
+  return halves_max(tree_max<ST * 16>(v));
+}
+
+// Online softmax of one step against the running reference m_used (base-2 units,
+// scale c = softmax scale * log2 e): the reference rises, and O and the sums are
+// rescaled, only when a row maximum grows by more than kLazyRescale, so most steps
+// skip the rescale.  Writes the step's weights exp2(c*s - m_used) to pb as bf16
+// (the B operand layout of pv_step) and adds them to the sums: r_part the rounded
+// weights that multiply V (PV), l_part the fp32 weights (LSE, or the energy sweep
+// without V).  O is normalised at the end by the rounded sum, so rounding the
+// weights perturbs a convex combination instead of scaling it.
+// EXT: one more running sum, x_part, rescaled and incremented like l_part (the
+// one-pass energy keeps the current key block's share there).
+template <int ST, int DT, bool PV, bool LSE, bool EXT = false>
+__device__ __forceinline__ void softmax_step(const f32x16* sacc, float c, float& m_used, float& l_part,
+                                             float& r_part, f32x16* oacc, bf16x8 (*pb)[2],
+                                             float* x_part = nullptr) {
+  const float mt = step_max<ST>(sacc) * c;
+  if (__ballot(mt > m_used + kLazyRescale)) {
+    asm volatile("" ::: "memory");  // rare: keep it a branch
+    const float m_new = fmaxf(m_used, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+    l_part *= alpha;
+    if (EXT) *x_part *= alpha;
+    r_part *= alpha;
+    if (PV) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    m_used = m_new;
+  }
+  float ps = 0.f;
+#pragma unroll
+  for (int t = 0; t < ST; ++t)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][k2 * 8 + e], c, -m_used));
+        if (LSE || !PV || EXT) ps += x;
+        if (PV) pb[t][k2][e] = (__bf16)x;
+      }
+  l_part += ps;
+  if (EXT) *x_part += ps;
+  if (PV) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int t = 0; t < ST; ++t)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pair = {pb[t][k2][e], pb[t][k2][e + 1]};
+          r_part = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, r_part, false);
+        }
+  }
+}
+
+// O^T += V^T P^T for one step: the V^T fragments come from the row-major V tile
+// through the LDS transpose read, with the key order of each fragment matched to
+// the order in which pb holds the weights.
+template <int D, int KT>
+__device__ __forceinline__ void pv_step(const bfraw* vt, const bf16x8 (*pb)[2], f32x16* oacc) {
+  constexpr int ST = KT / 32, DT = D / 32;
+  const int lane = threadIdx.x & 63, g = lane >> 5, G = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int t = 0; t < ST; ++t)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int krow = t * 32 + k2 * 16 + 4 * g + (li >> 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int dcol = dt * 32 + (G & 1) * 16 + 4 * (li & 3);
+        const i16x4 lo = lds_read_tr(vt + tile_off<D>(krow, dcol));
+        const i16x4 hi = lds_read_tr(vt + tile_off<D>(krow + 8, dcol));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[dt] = mfma(va, pb[t][k2], oacc[dt]);
+      }
+    }
+}
+
 }  // namespace dev
 }  // namespace cba

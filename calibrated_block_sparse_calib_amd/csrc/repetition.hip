@@ -112,25 +112,8 @@ __global__ __launch_bounds__(kRepGroups * NWV * 64, 2) void rep_sim_bf16_kernel(
     if (!active) continue;
     const int k0 = s * kKT;
     f32x16 sacc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sacc[t] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = lds_read8(kt + tile_off<D>(t * 32 + (lane & 31), ks * 16 + g * 8));
-        sacc[t] = mfma(a, qf[ks], sacc[t]);
-      }
-    }
-    if (k0 + kKT > p.n) {
-      // Ragged last step: element (t, i) holds key k0 + t*32 + (i/4)*8 + g*4 + i%4.
-      asm volatile("" ::: "memory");
-      const int lim = p.n - k0 - g * 4;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (t * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[t][i] = -INFINITY;
-    }
+    qk_step<D, kKT>(kt, qf, sacc);
+    if (k0 + kKT > p.n) mask_ragged<2>(sacc, p.n, k0);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
