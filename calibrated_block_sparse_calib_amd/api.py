@@ -150,7 +150,10 @@ def calib_block_energy_ws(q, k, v=None, *, block: int, n_prefix: int = 0, grid=N
                           workspace: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                           energy: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None):
     """calib_block_energy in one pass over the keys, using a workspace of
-    energy_workspace_bytes(q, block) bytes (allocated here when not given).
+    energy_workspace_bytes(q, block) bytes (allocated here when not given).  A
+    smaller workspace runs the pass in several launches with the same results; it
+    must hold at least one workgroup's rows (up to 8 query blocks x nb x block
+    floats).
     Returns (energy, lse, o); o is None without v."""
     _require_gpu(q, k, v, workspace, lse, energy, o)
     _same_layout(q, k, v, o)

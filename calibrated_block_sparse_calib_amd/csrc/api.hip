@@ -54,9 +54,14 @@ CBA_API cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* 
     return from_hip(cba::launch_energy_f32(p, desc->head_dim, desc->block, s));
   }
   const int64_t need = (int64_t)desc->batch * desc->heads * p.nb * p.nb * desc->block * (int64_t)sizeof(float);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return CBA_EINVAL;
-  if (workspace_bytes < need) return CBA_ECAPACITY;
-  return from_hip(cba::launch_energy1_bf16(p, desc->head_dim, desc->block, static_cast<float*>(workspace), -1, s));
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u) || workspace_bytes < 0) return CBA_EINVAL;
+  // A workspace smaller than the whole problem's runs the work in several launches
+  // over contiguous (batch item, head, query block) ranges; too small for one
+  // workgroup's rows is refused before anything is enqueued.
+  const hipError_t e = cba::launch_energy1_bf16(p, desc->head_dim, desc->block, static_cast<float*>(workspace),
+                                                workspace_bytes >= need ? -1 : workspace_bytes, s);
+  if (e == hipErrorInvalidValue) return CBA_ECAPACITY;
+  return from_hip(e);
 }
 
 CBA_API cba_status select_blocks_by_energy(const float* energy, int32_t n_draws, int32_t heads, int32_t nb,

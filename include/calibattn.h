@@ -95,9 +95,14 @@ cba_status calib_block_energy(const cba_attn_desc* desc, const void* q, const vo
  * (and dense_attn_fwd's); each energy entry is the sum of one tile in a fixed
  * order (repeated calls give identical bits; they may differ from
  * calib_block_energy's by rounding).
- *   workspace: device, 16-byte aligned, at least batch * heads * nb * nb * block
- *              floats (workspace_bytes); its contents on entry do not matter and
- *              are left undefined.  CBA_ECAPACITY when too small.
+ *   workspace: device, 16-byte aligned, workspace_bytes long; its contents on
+ *              entry do not matter and are left undefined.  With batch * heads *
+ *              nb * nb * block floats the pass runs in one launch; a smaller
+ *              workspace runs it in several launches over contiguous (batch item,
+ *              head, query block) ranges, each holding its rows' log-sums, with
+ *              bit-identical results.  CBA_ECAPACITY (nothing enqueued) when it
+ *              cannot hold one workgroup's rows (up to 8 query blocks x nb x block
+ *              floats).
  * fp32 inputs run the two sweeps and do not use the workspace. */
 cba_status calib_block_energy_ws(const cba_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
                                  float* lse, float* energy, void* workspace, int64_t workspace_bytes,

@@ -205,8 +205,11 @@ def test_energy_ws_rejects_bad_arguments(lib):
     d = _desc()  # bf16, 2 heads, 256 tokens, block 128: nb = 2, workspace 2*2*2*128*4 = 4096 bytes
     f = lib.calib_block_energy_ws
     assert f(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, None, 4096, None) == EINVAL  # no workspace
-    assert f(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 4095, None) == 4  # ECAPACITY
-    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4095, None) == 4  # with V too
+    # smaller than one workgroup's rows (two query blocks x nb x block floats = 2048 bytes): ECAPACITY
+    assert f(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 2047, None) == 4
+    # with V one query block per workgroup (1024 bytes)
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1023, None) == 4
+    assert f(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, -1, None) == EINVAL
     assert f(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, FAKE, 4096, None) == EINVAL  # no lse
     assert f(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4096, None) == EINVAL  # v without o
     assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == EINVAL  # o without v

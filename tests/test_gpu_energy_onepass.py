@@ -66,13 +66,34 @@ def test_onepass_energy_matches_oracle(d, block, grid, n_prefix):
     log(f"  ok max |dE| {worst:.2e}")
 
 
+@pytest.mark.parametrize("block,fraction", [(128, 0.999), (128, 0.3), (64, 0.25), (32, 0.2)])
+def test_onepass_partial_workspace_runs_in_chunks(block, fraction):
+    """A workspace smaller than the whole problem's runs the pass in several launches:
+    energies, LSE and O bit-identical to the single launch with a full workspace."""
+    cfg = _cfg(128, block, (2, 8, 16), 0)
+    draws = [make_qkv(cfg, draw=i) for i in range(2)]
+    dev = lambda i: torch.from_numpy(np.ascontiguousarray(np.stack([x[i] for x in draws]))).to(torch.bfloat16).cuda()
+    qd, kd, vd = dev(0), dev(1), dev(2)
+    need = cba.energy_workspace_bytes(qd, block)
+    for v in (None, vd):
+        e_full, l_full, o_full = cba.calib_block_energy_ws(qd, kd, v, block=block)
+        ws = torch.empty(int(need * fraction) // 16 * 16, dtype=torch.uint8, device="cuda")
+        e, l, o = cba.calib_block_energy_ws(qd, kd, v, block=block, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(e, e_full) and torch.equal(l, l_full)
+        if v is not None:
+            assert torch.equal(o, o_full)
+    log(f"  ok block {block}: workspace {fraction:.3f} of {need} bytes, bit-identical")
+
+
 def test_onepass_workspace_too_small_is_refused():
     cfg = _cfg(128, 128, (2, 8, 16), 0)
     q, k, _ = make_qkv(cfg, draw=0, with_v=False)
     qd = torch.from_numpy(q[None]).to(torch.bfloat16).cuda()
     kd = torch.from_numpy(k[None]).to(torch.bfloat16).cuda()
-    need = cba.energy_workspace_bytes(qd, 128)
-    ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    nb = cba.n_blocks(qd.shape[2], 128)
+    one_group = 2 * nb * 128 * 4  # two query blocks per workgroup without V
+    ws = torch.empty(one_group - 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(cba.CalibAttnError):
         cba.calib_block_energy_ws(qd, kd, block=128, workspace=ws)
 
