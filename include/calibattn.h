@@ -21,7 +21,8 @@
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates and
  *     frees every buffer; the library allocates nothing and keeps no state, so the
- *     calls are thread-safe.
+ *     calls are thread-safe.  The one exception is calib_block_energy_noalloc,
+ *     whose fixed per-GPU array is shared by its calls on that GPU (see there).
  *   - Each call validates its arguments on the host and either returns an error
  *     without enqueuing anything, or enqueues its kernels on `stream` and returns
  *     at once (no synchronisation).  Faults inside kernels surface at the
