@@ -58,8 +58,9 @@ typedef int32_t cba_status;
 #define CBA_DTYPE_F32 0
 #define CBA_DTYPE_BF16 1
 
-/* Shape and layout of one attention problem.  head_dim is 64 or 128; block is
- * 32, 64 or 128.  n_prefix must be a multiple of block.  grid_f*grid_h*grid_w is
+/* Shape and layout of one attention problem.  batch, heads and seq_len are at
+ * least 1 (an empty problem is CBA_EINVAL, not a no-op).  head_dim is 64 or 128;
+ * block is 32, 64 or 128.  n_prefix must be a multiple of block.  grid_f*grid_h*grid_w is
  * either 0 (no token grid: repetition heads are then not allowed) or
  * seq_len - n_prefix.  bf16 needs 16-byte aligned tensor pointers and strides
  * that are multiples of 8 elements. */
@@ -166,7 +167,7 @@ cba_status select_blocks_by_energy_heads(const float* energy, int32_t n_draws, i
 
 /* Skip list of a block mask in CSR form (zh S2.2B; pt S2A.5; fr S2C).
  *   mask: uint8 [n_rows, nkb] (1 = kept); for attention, n_rows = heads * nb and
- *         row r = h * nb + qb.
+ *         row r = h * nb + qb.  n_rows and nkb are at least 1 (CBA_EINVAL).
  *   row_ptr: int32 [n_rows + 1], row_ptr[0] = 0, row_ptr[r+1] - row_ptr[r] = kept
  *            blocks of row r.  Always written.
  *   col_idx: int32 [col_idx_capacity] or NULL.  NULL = count pass only.  Otherwise

@@ -71,6 +71,9 @@ FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced: validati
     (dict(head_dim=96), EUNSUPPORTED),
     (dict(block=48), EUNSUPPORTED),
     (dict(batch=0), EINVAL),
+    (dict(heads=0), EINVAL),
+    (dict(seq_len=0), EINVAL),
+    (dict(seq_len=-1), EINVAL),
     (dict(n_prefix=100), EINVAL),  # not a multiple of block
     (dict(grid_f=2, grid_h=2, grid_w=2), EINVAL),  # grid does not cover seq_len - n_prefix
     (dict(stride_n=64), EINVAL),  # rows overlap
@@ -121,6 +124,13 @@ def test_select_and_csr_reject_bad_sizes(lib):
     assert lib.build_block_csr(FAKE, 0, 4, FAKE, None, 0, None, None) == EINVAL
     assert lib.build_block_csr(FAKE, 4, 4, FAKE, FAKE, -1, None, None) == EINVAL
     assert lib.build_block_csr(FAKE, 1 << 20, 1 << 12, FAKE, None, 0, None, None) == EINVAL
+    # empty problems are rejected, not silently accepted
+    assert lib.build_block_csr(FAKE, 4, 0, FAKE, None, 0, None, None) == EINVAL
+    assert lib.build_block_intervals(FAKE, 0, 4, FAKE, None, 0, None) == EINVAL
+    assert lib.build_block_intervals(FAKE, 4, 0, FAKE, None, 0, None) == EINVAL
+    assert lib.order_heavy_rows_first(FAKE, 0, 4, 2.0, FAKE, None) == EINVAL
+    assert lib.select_blocks_by_energy(FAKE, 1, 0, 8, 0.9, 0.5, 1, 0, FAKE, None, None) == EINVAL
+    assert lib.select_blocks_by_energy(FAKE, 1, 1, 0, 0.9, 0.5, 1, 0, FAKE, None, None) == EINVAL
 
 
 def test_missing_library_raises(monkeypatch, tmp_path):
