@@ -190,7 +190,7 @@ def test_tiny_tau_one_is_dense(tiny):
 
 @pytest.mark.parametrize("draws,heads,nb,tau,rho,prefix", [
     (3, 2, 8, 0.9, 0.5, 0), (4, 3, 70, 0.95, 0.5, 2), (1, 1, 5, 0.5, 0.5, 0), (2, 2, 33, 1.0, 0.5, 0),
-    (4, 2, 591, 0.95, 0.5, 0), (4, 1, 929, 0.9, 0.49, 2)])
+    (4, 2, 591, 0.95, 0.5, 0), (4, 1, 929, 0.9, 0.49, 2), (1, 1, 4096, 0.95, 0.5, 0)])  # nb = 4096: the maximum
 def test_select_bitexact_on_same_energy(draws, heads, nb, tau, rho, prefix):
     rng = np.random.default_rng(nb * 7 + draws)
     e = (rng.random((draws, heads, nb, nb)) ** 6).astype(np.float32)
@@ -204,7 +204,7 @@ def test_select_bitexact_on_same_energy(draws, heads, nb, tau, rho, prefix):
 
 
 @pytest.mark.parametrize("rows,nkb,p", [(1, 1, 1.0), (16, 8, 0.4), (40, 591, 0.35), (300, 65, 0.5),
-                                        (7, 64, 0.0), (24, 929, 0.9), (1000, 129, 0.05)])
+                                        (7, 64, 0.0), (24, 929, 0.9), (1000, 129, 0.05), (6, 65535, 0.3)])
 def test_csr_bitexact(rows, nkb, p):
     rng = np.random.default_rng(rows + nkb)
     mask = (rng.random((rows, nkb)) < p).astype(np.uint8)
