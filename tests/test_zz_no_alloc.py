@@ -3,7 +3,8 @@ calib_block_energy_ws with a caller workspace: energies, LSE and O bit-identical
 on two calls in a row, the second on a smaller input.  The first input's
 workspace (338 MiB) exceeds the library's 256 MiB array, so that call runs in
 several launches; the second covers a batch of two, block 64 (two query blocks
-per workgroup) and a ragged last block."""
+per workgroup) and a ragged last block.  One call is also captured in a HIP graph
+and replayed, the use the entry point is for."""
 import numpy as np
 import pytest
 import torch
@@ -55,3 +56,29 @@ def test_noalloc_rejects_bad_arguments():
     q, k, _ = _inputs(1, 1, 256, 128, 4)
     with pytest.raises(cba.CalibAttnError):
         cba.calib_block_energy_noalloc(q, k[:, :, :200], block=128)
+
+
+def test_noalloc_under_graph_capture():
+    """The callers this entry point is for: one call captured in a HIP graph (after
+    an eager call, which looks up the array's address), replayed three times with
+    eager work between the replays (a fill of the outputs, and an eager call on
+    other inputs that reuses the array); every replay bit-identical to the eager
+    result."""
+    q, k, v = _inputs(1, 2, 3000, 128, 5)
+    e0, l0, o0 = cba.calib_block_energy_noalloc(q, k, v, block=128)
+    e, l, o = torch.empty_like(e0), torch.empty_like(l0), torch.empty_like(o0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cba.calib_block_energy_noalloc(q, k, v, block=128, lse=l, energy=e, o=o)
+    torch.cuda.synchronize()
+    for i in range(3):
+        e.fill_(-1.0)
+        l.fill_(-1.0)
+        o.fill_(-1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(e, e0) and torch.equal(l, l0) and torch.equal(o, o0), f"replay {i}"
+        cba.calib_block_energy_noalloc(k, q, None, block=128)
+        torch.cuda.synchronize()
+    log("  noalloc graph: 3 replays bit-identical to the eager call")
