@@ -31,6 +31,7 @@ CFLAGS = [
     "-fvisibility=hidden",
     "-Wall",
     "-Wno-unused-function",
+    "-Werror",  # host and device: a new warning fails the build
     # No packed fp32 instructions: keep fp32 math on the scalar-per-lane VALU forms.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",

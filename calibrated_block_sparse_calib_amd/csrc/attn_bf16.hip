@@ -218,7 +218,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, int row, int b, b
 // One workgroup per item: item i = blockIdx.x is row work_order[i / batch] (or
 // row i / batch when there is no order) and batch item i % batch.
 template <int D, int B, bool PV, bool LSE, bool BUF, bool IV>
-__global__ __launch_bounds__((Cfg<D, B>::NT), 2) void attn_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__((Cfg<D, B>::NT), (min_wgs_per_cu<D, Cfg<D, B>::NT>())) void attn_bf16_kernel(AttnParams p) {
   using C = Cfg<D, B>;
   __shared__ __attribute__((aligned(16))) bfraw k0s[C::TILE], k1s[C::TILE];
   __shared__ __attribute__((aligned(16))) bfraw v0s[PV ? C::TILE : 8], v1s[PV ? C::TILE : 8];

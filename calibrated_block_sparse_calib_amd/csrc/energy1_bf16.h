@@ -41,7 +41,7 @@ using namespace dev;
 // holds the workspace rows from ws_row0 on at ws, so a workspace smaller than the
 // whole problem can serve it in several launches.
 template <int D, int B, int QPB, bool PV, bool BUF>
-__global__ __launch_bounds__((QPB * Cfg<D, B>::NT), 2) void energy1_bf16_kernel(AttnParams p, float* ws,
+__global__ __launch_bounds__((QPB * Cfg<D, B>::NT), (min_wgs_per_cu<D, QPB * Cfg<D, B>::NT>())) void energy1_bf16_kernel(AttnParams p, float* ws,
                                                                                 int64_t item0, int64_t ws_row0) {
   using C = Cfg<D, B>;
   constexpr int NW = QPB * C::NW;  // waves per workgroup, 32 rows each

@@ -28,6 +28,16 @@ struct Cfg {
   static constexpr int ST = KT / 32;             // 32-key score tiles per step
 };
 
+// Workgroups per CU that the bf16 kernels ask the compiler to fit (launch
+// bounds).  Two for the tilings that reach two waves per SIMD; at head_dim 128
+// the one-wave workgroups of blocks 64 and 32 cannot (their double-buffered
+// tiles and registers allow one wave per SIMD), so they ask for one instead of
+// a target the compiler would miss.
+template <int D, int THREADS>
+constexpr int min_wgs_per_cu() {
+  return (D >= 128 && THREADS < 256) ? 1 : 2;
+}
+
 // Query blocks per energy workgroup: about 256 query rows (8 waves) share each K
 // tile, as far as the tile splits over the waves.
 template <int D, int B>
